@@ -1,0 +1,84 @@
+"""ctypes view of liblak.so (the C ABI declared in include/lak.h)."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblak.so")
+
+LAK_OK, LAK_EINVAL, LAK_ENOPAGE, LAK_EHIP, LAK_EUNSUPPORTED, LAK_ESTATE = 0, -1, -2, -3, -4, -5
+LAK_BF16, LAK_F32 = 0, 1
+LAK_AGG_MAX, LAK_AGG_SUM = 0, 1
+LAK_SCOPE_GROUP, LAK_SCOPE_ALL = 0, 1
+
+STATUS_NAMES = {0: "LAK_OK", -1: "LAK_EINVAL", -2: "LAK_ENOPAGE", -3: "LAK_EHIP", -4: "LAK_EUNSUPPORTED",
+                -5: "LAK_ESTATE"}
+
+
+class LakError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class CacheDesc(C.Structure):
+    _fields_ = [
+        ("num_layers", C.c_int32), ("max_batch", C.c_int32), ("num_q_heads", C.c_int32),
+        ("num_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("page_size", C.c_int32),
+        ("max_pages_per_seq", C.c_int32), ("dtype", C.c_int32), ("num_pages", C.c_int64),
+        ("k_pools", C.POINTER(C.c_void_p)), ("v_pools", C.POINTER(C.c_void_p)),
+        ("page_table", C.c_void_p), ("seq_lens", C.c_void_p),
+    ]
+
+
+_P = C.c_void_p
+_I32 = C.c_int32
+_I64 = C.c_int64
+_F = C.c_float
+_S = C.c_int  # lak_status
+
+# name -> (restype, argtypes); every symbol include/lak.h declares
+SIGNATURES = {
+    "lak_pool_bytes": (_I64, [C.POINTER(CacheDesc)]),
+    "lak_cache_create": (_S, [C.POINTER(CacheDesc), C.POINTER(_P)]),
+    "lak_cache_destroy": (_S, [_P]),
+    "lak_seq_reset": (_S, [_P, _I32, C.POINTER(_I32), _I32, _P]),
+    "lak_step_begin": (_S, [_P, _P]),
+    "lak_seq_lens_host": (_S, [_P, C.POINTER(_I32), _I32, C.POINTER(_I32)]),
+    "lak_page_table_host": (_S, [_P, _I32, C.POINTER(_I32), _I32, C.POINTER(_I32)]),
+    "lak_free_pages": (_I64, [_P]),
+    "lak_workspace_bytes": (C.c_size_t, [_P]),
+    "lak_kv_append": (_S, [_P, _I32, _P, _P, _P]),
+    "lak_kv_prefill": (_S, [_P, _I32, _P, _P, _I64, _P]),
+    "lak_kv_write_rows": (_S, [_P, _I32, _I32, _P, _P, _P, _P]),
+    "lak_kv_gather": (_S, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    "lak_attn_full": (_S, [_P, _I32, _P, _F, _P, _P, _P, C.c_size_t, _P]),
+    "lak_attn_delta_select": (_S, [_P, _I32, _P, _F, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _I32, _P, _P,
+                                   C.c_size_t, _P]),
+    "lak_page_select": (_S, [_P, _P, _I32, _I32, _I32, _P, _P, _I32, _P]),
+    "lak_attn_sparse": (_S, [_P, _I32, _P, _F, _P, _P, _I32, _I32, _P, _P, _P, C.c_size_t, _P]),
+    "lak_last_error": (C.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if the HIP build is missing (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m layer_aware_kv_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def check(status: int, where: str):
+    if status != LAK_OK:
+        raise LakError(status, where, lib().lak_last_error().decode())

@@ -1,0 +1,542 @@
+// C ABI of the layer-aware KV decode-attention library: argument validation, the
+// host page allocator, workspace layout, split planning and kernel launches.
+// See include/lak.h for the contract of every entry point.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "lak.h"
+#include "lak_internal.h"
+
+using namespace lak;
+
+namespace {
+
+thread_local std::string g_err;
+
+lak_status fail(lak_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+// Success leaves the last error message in place (it describes the last failure).
+lak_status ok() { return LAK_OK; }
+
+lak_status hip_fail(hipError_t e, const char* where) {
+  return fail(LAK_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// Workgroups a split-K launch aims for (about 4 per compute unit on a 256-CU part)
+// and the fewest 16-token sub-tiles one workgroup is given.
+constexpr int kTargetWgs = 1024;
+constexpr int kMinSubtilesPerWg = 8;
+constexpr int kScoreTokensPerBlock = 2048;
+
+int esize(int dtype) { return dtype == LAK_BF16 ? 2 : 4; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+struct lak_cache {
+  lak_cache_desc d;
+  std::vector<void*> kp, vp;
+  bool host_only = false;
+  int batch = -1;
+  std::vector<int32_t> lens;
+  std::vector<std::vector<int32_t>> pages;
+  std::vector<int32_t> free_list;  // stack; back() is handed out next
+  std::vector<int32_t> table_staging;
+  std::vector<int32_t> lens_staging;
+  int s_cap = 0;
+
+  int max_np() const {
+    int m = 0;
+    for (int b = 0; b < batch; ++b) m = std::max(m, (lens[b] + d.page_size - 1) / d.page_size);
+    return m;
+  }
+  int max_len() const {
+    int m = 0;
+    for (int b = 0; b < batch; ++b) m = std::max(m, lens[b]);
+    return m;
+  }
+  void reset_free_list() {
+    free_list.clear();
+    free_list.reserve((size_t)d.num_pages);
+    for (int64_t p = d.num_pages - 1; p >= 0; --p) free_list.push_back((int32_t)p);
+    for (auto& v : pages) v.clear();
+  }
+};
+
+namespace {
+
+struct WsLayout {
+  size_t o_part, ml_part, lse, logits, scores, total;
+};
+
+WsLayout ws_layout(const lak_cache* c) {
+  const auto& d = c->d;
+  WsLayout w;
+  size_t off = 0;
+  const size_t rows_h = (size_t)d.max_batch * d.num_q_heads;
+  w.o_part = off;
+  off = align256(off + rows_h * c->s_cap * d.head_dim * sizeof(float));
+  w.ml_part = off;
+  off = align256(off + rows_h * c->s_cap * 2 * sizeof(float));
+  w.lse = off;
+  off = align256(off + rows_h * sizeof(float));
+  w.logits = off;
+  off = align256(off + rows_h * (size_t)d.max_pages_per_seq * d.page_size * sizeof(float));
+  w.scores = off;
+  off = align256(off + (size_t)d.max_batch * d.num_kv_heads * d.max_pages_per_seq * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+// Items (pages or selection entries) per split for `rows` rows of up to
+// `max_items` items each.
+int plan_pps(int rows, int max_items, int subtiles_per_page) {
+  const int64_t work = (int64_t)rows * max_items;
+  int pps = (int)((work + kTargetWgs - 1) / kTargetWgs);
+  const int min_pps = (kMinSubtilesPerWg + subtiles_per_page - 1) / subtiles_per_page;
+  return std::max(std::max(pps, min_pps), 1);
+}
+
+lak_status check_cache(const lak_cache* c, bool need_device) {
+  if (!c) return fail(LAK_EINVAL, "cache is NULL");
+  if (c->batch < 0) return fail(LAK_ESTATE, "no active batch: call lak_seq_reset first");
+  if (need_device && c->host_only) return fail(LAK_ESTATE, "metadata-only cache has no device buffers");
+  return LAK_OK;
+}
+
+lak_status check_layer(const lak_cache* c, int layer) {
+  if (layer < 0 || layer >= c->d.num_layers)
+    return fail(LAK_EINVAL, "layer %d out of range [0, %d)", layer, c->d.num_layers);
+  if (!c->kp[layer] || !c->vp[layer]) return fail(LAK_EINVAL, "pool of layer %d is NULL", layer);
+  return LAK_OK;
+}
+
+KvGeom geom(const lak_cache* c) {
+  KvGeom g;
+  g.hkv = c->d.num_kv_heads;
+  g.d = c->d.head_dim;
+  g.page = c->d.page_size;
+  g.max_pages = c->d.max_pages_per_seq;
+  g.esz = esize(c->d.dtype);
+  return g;
+}
+
+lak_status check_ws(const lak_cache* c, const void* ws, size_t ws_bytes) {
+  const size_t need = ws_layout(c).total;
+  if (!ws) return fail(LAK_EINVAL, "workspace is NULL");
+  if (ws_bytes < need) return fail(LAK_EINVAL, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  if (((uintptr_t)ws & 255) != 0) return fail(LAK_EINVAL, "workspace not 256-byte aligned");
+  return LAK_OK;
+}
+
+// Runs the split-K decode plus combine of one tier.
+lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, float sm_scale,
+                         void* out, float* lse, const int32_t* sel, const int32_t* sel_count,
+                         int sel_cap, int sel_rows, void* ws, hipStream_t st) {
+  const auto& d = c->d;
+  const WsLayout w = ws_layout(c);
+  char* wsb = static_cast<char*>(ws);
+  const int spp = d.page_size / 16;
+  int max_items = c->max_np();
+  if (mode == MODE_SPARSE) max_items = std::min(max_items, sel_cap);
+  const int rows = c->batch * d.num_kv_heads;
+  const int pps = plan_pps(rows, max_items, spp);
+  const int splits = (max_items + pps - 1) / pps;
+  if (splits > c->s_cap) return fail(LAK_EINVAL, "internal: %d splits exceed capacity %d", splits, c->s_cap);
+
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.k_pool = c->kp[layer];
+  a.v_pool = c->vp[layer];
+  a.page_table = d.page_table;
+  a.seq_lens = d.seq_lens;
+  a.q = q;
+  a.sm_scale = sm_scale;
+  a.hq = d.num_q_heads;
+  a.hkv = d.num_kv_heads;
+  a.page = d.page_size;
+  a.max_pages = d.max_pages_per_seq;
+  a.pps = pps;
+  a.s_cap = c->s_cap;
+  a.sel = sel;
+  a.sel_count = sel_count;
+  a.sel_cap = sel_cap;
+  a.sel_rows = sel_rows;
+  a.o_part = reinterpret_cast<float*>(wsb + w.o_part);
+  a.ml_part = reinterpret_cast<float*>(wsb + w.ml_part);
+  a.logits = reinterpret_cast<float*>(wsb + w.logits);
+  a.t_pad = (int64_t)d.max_pages_per_seq * d.page_size;
+  hipError_t e = launch_decode(d.dtype, mode, d.head_dim, a, splits, c->batch, st);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+
+  CombineArgs cb;
+  std::memset(&cb, 0, sizeof(cb));
+  cb.o_part = a.o_part;
+  cb.ml_part = a.ml_part;
+  cb.seq_lens = d.seq_lens;
+  cb.sel_count = (mode == MODE_SPARSE) ? sel_count : nullptr;
+  cb.sel_cap = sel_cap;
+  cb.sel_rows = sel_rows;
+  cb.hq = d.num_q_heads;
+  cb.hkv = d.num_kv_heads;
+  cb.page = d.page_size;
+  cb.pps = pps;
+  cb.s_cap = c->s_cap;
+  cb.splits = splits;
+  cb.out = out;
+  cb.lse = lse;
+  cb.lse2 = (mode == MODE_DELTA) ? reinterpret_cast<float*>(wsb + w.lse) : nullptr;
+  e = launch_combine(d.dtype, d.head_dim, cb, c->batch, st);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return ok();
+}
+
+lak_status run_select(lak_cache* c, const float* scores, int scope, int k_top, int recency,
+                      int32_t* sel, int32_t* sel_count, int sel_cap, hipStream_t st) {
+  TopkArgs t;
+  t.scores = scores;
+  t.seq_lens = c->d.seq_lens;
+  t.sel = sel;
+  t.sel_count = sel_count;
+  t.rows_per_seq = scope == LAK_SCOPE_GROUP ? c->d.num_kv_heads : 1;
+  t.page = c->d.page_size;
+  t.max_pages = c->d.max_pages_per_seq;
+  t.k_top = k_top;
+  t.recency = recency;
+  t.sel_cap = sel_cap;
+  hipError_t e = launch_topk(t, c->batch, st);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  return ok();
+}
+
+lak_status check_select_args(const lak_cache* c, int scope, int k_top, int recency, const int32_t* sel,
+                             const int32_t* sel_count, int sel_cap) {
+  if (scope != LAK_SCOPE_GROUP && scope != LAK_SCOPE_ALL) return fail(LAK_EINVAL, "bad scope %d", scope);
+  if (k_top < 0 || recency < 0) return fail(LAK_EINVAL, "k_top and recency must be >= 0");
+  if ((int64_t)k_top + recency > sel_cap)
+    return fail(LAK_EINVAL, "sel_capacity %d < k_top + recency = %lld", sel_cap, (long long)k_top + recency);
+  if (!sel || !sel_count) return fail(LAK_EINVAL, "sel / sel_count is NULL");
+  (void)c;
+  return LAK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t lak_pool_bytes(const lak_cache_desc* d) {
+  if (!d || d->num_pages <= 0 || d->num_kv_heads <= 0 || d->page_size <= 0 || d->head_dim <= 0 ||
+      (d->dtype != LAK_BF16 && d->dtype != LAK_F32))
+    return -1;
+  return d->num_pages * d->num_kv_heads * (int64_t)d->page_size * d->head_dim * esize(d->dtype);
+}
+
+lak_status lak_cache_create(const lak_cache_desc* desc, lak_cache** out) {
+  if (!desc || !out) return fail(LAK_EINVAL, "desc/out is NULL");
+  const lak_cache_desc& d = *desc;
+  if (d.num_layers <= 0 || d.max_batch <= 0 || d.num_q_heads <= 0 || d.num_kv_heads <= 0 ||
+      d.head_dim <= 0 || d.page_size <= 0 || d.max_pages_per_seq <= 0 || d.num_pages <= 0)
+    return fail(LAK_EINVAL, "all sizes must be positive");
+  if (d.num_q_heads % d.num_kv_heads != 0)
+    return fail(LAK_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", d.num_q_heads, d.num_kv_heads);
+  if (d.dtype != LAK_BF16 && d.dtype != LAK_F32) return fail(LAK_EINVAL, "bad dtype %d", d.dtype);
+  if (d.num_pages > 0x7FFFFFFF) return fail(LAK_EINVAL, "num_pages exceeds int32 page ids");
+  const int G = d.num_q_heads / d.num_kv_heads;
+  if (G > 16) return fail(LAK_EUNSUPPORTED, "group size %d > 16", G);
+  if (d.head_dim != 64 && d.head_dim != 128) return fail(LAK_EUNSUPPORTED, "head_dim %d (built: 64, 128)", d.head_dim);
+  if (d.page_size != 16 && d.page_size != 32 && d.page_size != 64)
+    return fail(LAK_EUNSUPPORTED, "page_size %d (built: 16, 32, 64)", d.page_size);
+  if ((int64_t)d.max_pages_per_seq * d.page_size > 0x7FFFFFFF)
+    return fail(LAK_EINVAL, "max_pages_per_seq * page_size exceeds int32 positions");
+  const bool host_only = !d.page_table && !d.seq_lens;
+  if (!host_only) {
+    if (!d.page_table || !d.seq_lens) return fail(LAK_EINVAL, "page_table and seq_lens must both be set");
+    if (!d.k_pools || !d.v_pools) return fail(LAK_EINVAL, "k_pools / v_pools arrays are NULL");
+  }
+  lak_cache* c = new lak_cache();
+  c->d = d;
+  c->host_only = host_only;
+  c->kp.assign(d.num_layers, nullptr);
+  c->vp.assign(d.num_layers, nullptr);
+  if (!host_only)
+    for (int l = 0; l < d.num_layers; ++l) {
+      c->kp[l] = d.k_pools[l];
+      c->vp[l] = d.v_pools[l];
+    }
+  c->d.k_pools = nullptr;
+  c->d.v_pools = nullptr;
+  c->pages.resize(d.max_batch);
+  c->lens.assign(d.max_batch, 0);
+  c->reset_free_list();
+  c->s_cap = std::min((kTargetWgs + d.num_kv_heads - 1) / d.num_kv_heads, d.max_pages_per_seq);
+  *out = c;
+  return ok();
+}
+
+lak_status lak_cache_destroy(lak_cache* c) {
+  delete c;
+  return ok();
+}
+
+lak_status lak_seq_reset(lak_cache* c, int32_t batch, const int32_t* host_lens, int32_t reserve_tokens,
+                         void* stream) {
+  if (!c) return fail(LAK_EINVAL, "cache is NULL");
+  if (batch < 0 || batch > c->d.max_batch) return fail(LAK_EINVAL, "batch %d outside [0, %d]", batch, c->d.max_batch);
+  if (batch > 0 && !host_lens) return fail(LAK_EINVAL, "host_lens is NULL");
+  if (reserve_tokens < 0) return fail(LAK_EINVAL, "reserve_tokens < 0");
+  const int P = c->d.page_size;
+  int64_t need = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (host_lens[b] < 0) return fail(LAK_EINVAL, "host_lens[%d] < 0", b);
+    const int64_t np = ((int64_t)host_lens[b] + reserve_tokens + P - 1) / P;
+    if (np > c->d.max_pages_per_seq)
+      return fail(LAK_EINVAL, "sequence %d needs %lld pages > max_pages_per_seq %d", b, (long long)np,
+                  c->d.max_pages_per_seq);
+    need += np;
+  }
+  c->batch = -1;
+  c->reset_free_list();
+  if (need > (int64_t)c->free_list.size())
+    return fail(LAK_ENOPAGE, "batch needs %lld pages, pool has %lld", (long long)need, (long long)c->d.num_pages);
+  for (int b = 0; b < batch; ++b) {
+    const int np = (int)(((int64_t)host_lens[b] + reserve_tokens + P - 1) / P);
+    c->pages[b].resize(np);
+    for (int i = 0; i < np; ++i) {
+      c->pages[b][i] = c->free_list.back();
+      c->free_list.pop_back();
+    }
+    c->lens[b] = host_lens[b];
+  }
+  c->batch = batch;
+  if (c->host_only || batch == 0) return ok();
+  const int mp = c->d.max_pages_per_seq;
+  c->table_staging.assign((size_t)batch * mp, 0);
+  for (int b = 0; b < batch; ++b)
+    std::copy(c->pages[b].begin(), c->pages[b].end(), c->table_staging.begin() + (size_t)b * mp);
+  c->lens_staging.assign(c->lens.begin(), c->lens.begin() + batch);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(c->d.page_table, c->table_staging.data(), c->table_staging.size() * 4,
+                                hipMemcpyHostToDevice, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(c->d.seq_lens, c->lens_staging.data(), c->lens_staging.size() * 4,
+                       hipMemcpyHostToDevice, st);
+  // the staging vectors must outlive the copies
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "page table upload");
+  return ok();
+}
+
+lak_status lak_step_begin(lak_cache* c, void* stream) {
+  lak_status s = check_cache(c, false);
+  if (s != LAK_OK) return s;
+  const int P = c->d.page_size;
+  // plan first: nothing changes unless every sequence gets its page
+  std::vector<int> needs;
+  for (int b = 0; b < c->batch; ++b) {
+    const int t = c->lens[b] + 1;
+    const int np = (t + P - 1) / P;
+    if (np > c->d.max_pages_per_seq)
+      return fail(LAK_EINVAL, "sequence %d would exceed max_pages_per_seq %d", b, c->d.max_pages_per_seq);
+    if (np > (int)c->pages[b].size()) needs.push_back(b);
+  }
+  if (needs.size() > c->free_list.size())
+    return fail(LAK_ENOPAGE, "step needs %zu new pages, %zu free", needs.size(), c->free_list.size());
+  std::vector<int32_t> nb, nlp, npg;
+  for (int b : needs) {
+    const int32_t p = c->free_list.back();
+    c->free_list.pop_back();
+    nb.push_back(b);
+    nlp.push_back((int32_t)c->pages[b].size());
+    npg.push_back(p);
+    c->pages[b].push_back(p);
+  }
+  for (int b = 0; b < c->batch; ++b) c->lens[b] += 1;
+  if (c->host_only) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  size_t i = 0;
+  do {
+    StepUpdate u;
+    std::memset(&u, 0, sizeof(u));
+    u.n = (int32_t)std::min<size_t>(kStepMax, nb.size() - i);
+    for (int k = 0; k < u.n; ++k) {
+      u.b[k] = nb[i + k];
+      u.lp[k] = nlp[i + k];
+      u.page[k] = npg[i + k];
+    }
+    i += u.n;
+    u.batch = (i >= nb.size()) ? c->batch : 0;
+    hipError_t e = launch_step_update(u, c->d.page_table, c->d.seq_lens, c->d.max_pages_per_seq, st);
+    if (e != hipSuccess) return hip_fail(e, "step update launch");
+  } while (i < nb.size());
+  return ok();
+}
+
+lak_status lak_seq_lens_host(const lak_cache* c, int32_t* out, int32_t cap, int32_t* batch) {
+  if (!c || !out) return fail(LAK_EINVAL, "NULL argument");
+  const int B = std::max(c->batch, 0);
+  if (cap < B) return fail(LAK_EINVAL, "cap %d < batch %d", cap, B);
+  for (int b = 0; b < B; ++b) out[b] = c->lens[b];
+  if (batch) *batch = c->batch;
+  return ok();
+}
+
+lak_status lak_page_table_host(const lak_cache* c, int32_t b, int32_t* out, int32_t cap, int32_t* n_pages) {
+  if (!c || !out || !n_pages) return fail(LAK_EINVAL, "NULL argument");
+  if (b < 0 || b >= c->batch) return fail(LAK_EINVAL, "sequence %d not active", b);
+  const auto& v = c->pages[b];
+  *n_pages = (int32_t)v.size();
+  for (int i = 0; i < (int)v.size() && i < cap; ++i) out[i] = v[i];
+  return ok();
+}
+
+int64_t lak_free_pages(const lak_cache* c) { return c ? (int64_t)c->free_list.size() : -1; }
+
+size_t lak_workspace_bytes(const lak_cache* c) { return c ? ws_layout(c).total : 0; }
+
+lak_status lak_kv_append(lak_cache* c, int32_t layer, const void* k_new, const void* v_new, void* stream) {
+  lak_status s = check_cache(c, true);
+  if (s != LAK_OK) return s;
+  if ((s = check_layer(c, layer)) != LAK_OK) return s;
+  if (c->batch == 0) return ok();
+  if (!k_new || !v_new) return fail(LAK_EINVAL, "k_new / v_new is NULL");
+  hipError_t e = launch_append(geom(c), c->kp[layer], c->vp[layer], c->d.page_table, c->d.seq_lens, k_new,
+                               v_new, c->batch, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ok();
+}
+
+lak_status lak_kv_prefill(lak_cache* c, int32_t layer, const void* k, const void* v, int64_t t_stride,
+                          void* stream) {
+  lak_status s = check_cache(c, true);
+  if (s != LAK_OK) return s;
+  if ((s = check_layer(c, layer)) != LAK_OK) return s;
+  if (c->batch == 0) return ok();
+  if (!k || !v) return fail(LAK_EINVAL, "k / v is NULL");
+  const int mt = c->max_len();
+  if (t_stride < mt) return fail(LAK_EINVAL, "t_stride %lld < longest sequence %d", (long long)t_stride, mt);
+  hipError_t e = launch_prefill(geom(c), c->kp[layer], c->vp[layer], c->d.page_table, c->d.seq_lens, k, v,
+                                t_stride, c->batch, mt, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return ok();
+}
+
+lak_status lak_kv_write_rows(lak_cache* c, int32_t layer, int32_t n, const int32_t* rows, const void* k_rows,
+                             const void* v_rows, void* stream) {
+  lak_status s = check_cache(c, true);
+  if (s != LAK_OK) return s;
+  if ((s = check_layer(c, layer)) != LAK_OK) return s;
+  if (n < 0) return fail(LAK_EINVAL, "n < 0");
+  if (n > 0 && (!rows || !k_rows)) return fail(LAK_EINVAL, "rows / k_rows is NULL");
+  hipError_t e = launch_write_rows(geom(c), c->kp[layer], c->vp[layer], c->d.page_table, c->d.seq_lens, n, rows,
+                                   k_rows, v_rows, c->batch, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "write_rows launch");
+  return ok();
+}
+
+lak_status lak_kv_gather(lak_cache* c, int32_t layer, int32_t b, int32_t g, int32_t t0, int32_t n, void* k_out,
+                         void* v_out, void* stream) {
+  lak_status s = check_cache(c, true);
+  if (s != LAK_OK) return s;
+  if ((s = check_layer(c, layer)) != LAK_OK) return s;
+  if (b < 0 || b >= c->batch) return fail(LAK_EINVAL, "sequence %d not active", b);
+  if (g < 0 || g >= c->d.num_kv_heads) return fail(LAK_EINVAL, "kv head %d out of range", g);
+  if (t0 < 0 || n < 0 || (int64_t)t0 + n > c->lens[b])
+    return fail(LAK_EINVAL, "tokens [%d, %lld) outside [0, %d)", t0, (long long)t0 + n, c->lens[b]);
+  hipError_t e = launch_gather(geom(c), c->kp[layer], c->vp[layer], c->d.page_table, b, g, t0, n, k_out, v_out,
+                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return ok();
+}
+
+lak_status lak_attn_full(lak_cache* c, int32_t layer, const void* q, float sm_scale, void* out, float* lse,
+                         void* ws, size_t ws_bytes, void* stream) {
+  lak_status s = check_cache(c, true);
+  if (s != LAK_OK) return s;
+  if ((s = check_layer(c, layer)) != LAK_OK) return s;
+  if (c->batch == 0) return ok();
+  if (!q || !out) return fail(LAK_EINVAL, "q / out is NULL");
+  if ((s = check_ws(c, ws, ws_bytes)) != LAK_OK) return s;
+  return run_attention(c, layer, MODE_FULL, q, sm_scale, out, lse, nullptr, nullptr, 0, 1, ws,
+                       static_cast<hipStream_t>(stream));
+}
+
+lak_status lak_attn_delta_select(lak_cache* c, int32_t layer, const void* q, float sm_scale, void* out,
+                                 float* lse, int32_t k_top, int32_t recency, int32_t agg, int32_t scope,
+                                 int32_t* sel, int32_t* sel_count, int32_t sel_capacity, float* page_scores,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  lak_status s = check_cache(c, true);
+  if (s != LAK_OK) return s;
+  if ((s = check_layer(c, layer)) != LAK_OK) return s;
+  if (!q || !out) return fail(LAK_EINVAL, "q / out is NULL");
+  if (agg != LAK_AGG_MAX && agg != LAK_AGG_SUM) return fail(LAK_EINVAL, "bad agg %d", agg);
+  if ((s = check_select_args(c, scope, k_top, recency, sel, sel_count, sel_capacity)) != LAK_OK) return s;
+  if (c->batch == 0) return ok();
+  if ((s = check_ws(c, ws, ws_bytes)) != LAK_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  s = run_attention(c, layer, MODE_DELTA, q, sm_scale, out, lse, nullptr, nullptr, 0, 1, ws, st);
+  if (s != LAK_OK) return s;
+  const WsLayout w = ws_layout(c);
+  char* wsb = static_cast<char*>(ws);
+  float* scores = page_scores ? page_scores : reinterpret_cast<float*>(wsb + w.scores);
+  PageScoreArgs pa;
+  pa.logits = reinterpret_cast<const float*>(wsb + w.logits);
+  pa.lse = reinterpret_cast<const float*>(wsb + w.lse);
+  pa.seq_lens = c->d.seq_lens;
+  pa.scores = scores;
+  pa.t_pad = (int64_t)c->d.max_pages_per_seq * c->d.page_size;
+  pa.hq = c->d.num_q_heads;
+  pa.hkv = c->d.num_kv_heads;
+  pa.page = c->d.page_size;
+  pa.max_pages = c->d.max_pages_per_seq;
+  pa.agg = agg;
+  pa.scope = scope;
+  pa.tokens_per_block = kScoreTokensPerBlock;
+  const int rows = scope == LAK_SCOPE_GROUP ? c->d.num_kv_heads : 1;
+  hipError_t e = launch_page_score(pa, c->batch, rows, c->max_np(), st);
+  if (e != hipSuccess) return hip_fail(e, "page score launch");
+  return run_select(c, scores, scope, k_top, recency, sel, sel_count, sel_capacity, st);
+}
+
+lak_status lak_page_select(lak_cache* c, const float* page_scores, int32_t scope, int32_t k_top, int32_t recency,
+                           int32_t* sel, int32_t* sel_count, int32_t sel_capacity, void* stream) {
+  lak_status s = check_cache(c, true);
+  if (s != LAK_OK) return s;
+  if (!page_scores) return fail(LAK_EINVAL, "page_scores is NULL");
+  if ((s = check_select_args(c, scope, k_top, recency, sel, sel_count, sel_capacity)) != LAK_OK) return s;
+  return run_select(c, page_scores, scope, k_top, recency, sel, sel_count, sel_capacity,
+                    static_cast<hipStream_t>(stream));
+}
+
+lak_status lak_attn_sparse(lak_cache* c, int32_t layer, const void* q, float sm_scale, const int32_t* sel,
+                           const int32_t* sel_count, int32_t sel_capacity, int32_t scope, void* out, float* lse,
+                           void* ws, size_t ws_bytes, void* stream) {
+  lak_status s = check_cache(c, true);
+  if (s != LAK_OK) return s;
+  if ((s = check_layer(c, layer)) != LAK_OK) return s;
+  if (c->batch == 0) return ok();
+  if (!q || !out) return fail(LAK_EINVAL, "q / out is NULL");
+  if (!sel || !sel_count) return fail(LAK_EINVAL, "sel / sel_count is NULL");
+  if (sel_capacity <= 0) return fail(LAK_EINVAL, "sel_capacity must be > 0");
+  if (scope != LAK_SCOPE_GROUP && scope != LAK_SCOPE_ALL) return fail(LAK_EINVAL, "bad scope %d", scope);
+  if ((s = check_ws(c, ws, ws_bytes)) != LAK_OK) return s;
+  const int sel_rows = scope == LAK_SCOPE_GROUP ? c->d.num_kv_heads : 1;
+  return run_attention(c, layer, MODE_SPARSE, q, sm_scale, out, lse, sel, sel_count, sel_capacity, sel_rows, ws,
+                       static_cast<hipStream_t>(stream));
+}
+
+const char* lak_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

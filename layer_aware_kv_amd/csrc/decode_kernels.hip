@@ -1,0 +1,372 @@
+// Split-K decode attention over the paged KV cache, for the three layer tiers of
+// DELTA ("Methodology in Plain English", DELTA AI summary page):
+//   MODE_FULL   full attention (layers 0-1),
+//   MODE_DELTA  full attention that also writes the scaled logits of every valid
+//               token (the delta-layer scores are taken from the decode kernel's
+//               own logits, as the pages' implementation does),
+//   MODE_SPARSE attention over the tokens of the selected pages only.
+// One workgroup = one (sequence b, KV head g, split s); its 4 waves take the 16-token
+// sub-tiles of the split in turn.  Per sub-tile: S^T = K Q^T with the G query heads
+// of the group as the 16-wide MFMA N dimension, online softmax in the log2
+// domain, then O^T += V^T P^T.  K and V fragments come straight from HBM into
+// registers (the pool's in-page order matches the MFMA operand layout, so every
+// load instruction is one contiguous 1 KiB).  Waves merge through LDS; the split
+// partials (o, max, sum) are merged by combine_kernel.
+#include <math.h>
+
+#include "lak_device.h"
+#include "lak_internal.h"
+
+namespace lak {
+
+template <int ESZ, int D>
+struct Frag;
+
+// bfloat16: q.K^T with v_mfma_f32_16x16x32_bf16 (D/32 per sub-tile), P.V with
+// v_mfma_f32_16x16x16_bf16 (D/16 per sub-tile).
+template <int D>
+struct Frag<2, D> {
+  static constexpr int NL = D / 32;  // 16-byte loads per lane per operand
+  static constexpr int NO = D / 16;  // 16-row output tiles of O^T
+  u32x4 k[NL], v[NL];
+  typedef bf16x8 QF;
+
+  __device__ inline void load(const uint16_t* kb, const uint16_t* vb, int lane) {
+    const u32x4* kp = reinterpret_cast<const u32x4*>(kb);
+    const u32x4* vp = reinterpret_cast<const u32x4*>(vb);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) k[i] = kp[i * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) v[i] = vp[i * 64 + lane];
+  }
+  // lane l: head l%16, head-dim chunk (4i + l/16)*8 .. +8
+  __device__ static inline void load_q(QF* qf, const uint16_t* qrow, bool valid, int j) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (valid) w = *reinterpret_cast<const u32x4*>(qrow + 32 * i + 8 * j);
+      qf[i] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  __device__ inline f32x4 qk(const QF* qf) const {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k[i]), qf[i], s, 0, 0, 0);
+    return s;
+  }
+  // zero the V elements of tokens >= nvalid (token of element x is 4(l/16) + x%4)
+  __device__ inline void mask_v(int nvalid, int j) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (4 * j + e >= nvalid) {
+        const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          v[i][e >> 1] &= keep;
+          v[i][2 + (e >> 1)] &= keep;
+        }
+      }
+    }
+  }
+  __device__ inline void pv(f32x4* o, const float* p) const {
+    const uint32_t w0 = (uint32_t)f32_to_bf16_rne(p[0]) | ((uint32_t)f32_to_bf16_rne(p[1]) << 16);
+    const uint32_t w1 = (uint32_t)f32_to_bf16_rne(p[2]) | ((uint32_t)f32_to_bf16_rne(p[3]) << 16);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const i16x4 pf = __builtin_bit_cast(i16x4, (u32x2){w0, w1});
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const i16x4 va = __builtin_bit_cast(i16x4, (u32x2){v[i][0], v[i][1]});
+      const i16x4 vb = __builtin_bit_cast(i16x4, (u32x2){v[i][2], v[i][3]});
+      o[2 * i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pf, o[2 * i], 0, 0, 0);
+      o[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vb, pf, o[2 * i + 1], 0, 0, 0);
+    }
+  }
+};
+
+// float32: v_mfma_f32_16x16x4_f32 for both products (D/4 each per sub-tile).
+template <int D>
+struct Frag<4, D> {
+  static constexpr int NL = D / 16;
+  static constexpr int NO = D / 16;
+  u32x4 k[NL], v[NL];
+  typedef f32x4 QF;
+
+  __device__ inline void load(const uint32_t* kb, const uint32_t* vb, int lane) {
+    const u32x4* kp = reinterpret_cast<const u32x4*>(kb);
+    const u32x4* vp = reinterpret_cast<const u32x4*>(vb);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) k[i] = kp[i * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) v[i] = vp[i * 64 + lane];
+  }
+  // lane l: head l%16, head-dim elements 16i + 4(l/16) .. +4
+  __device__ static inline void load_q(QF* qf, const uint32_t* qrow, bool valid, int j) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      f32x4 w = {0.f, 0.f, 0.f, 0.f};
+      if (valid) w = *reinterpret_cast<const f32x4*>(qrow + 16 * i + 4 * j);
+      qf[i] = w;
+    }
+  }
+  __device__ inline f32x4 qk(const QF* qf) const {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k[i][e]), qf[i][e], s, 0, 0, 0);
+    return s;
+  }
+  __device__ inline void mask_v(int nvalid, int j) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * j + e >= nvalid) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) v[i][e] = 0u;
+      }
+  }
+  __device__ inline void pv(f32x4* o, const float* p) const {
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v[i][e]), p[e], o[i], 0, 0, 0);
+  }
+};
+
+template <int ESZ>
+struct ElemT;
+template <>
+struct ElemT<2> { typedef uint16_t T; };
+template <>
+struct ElemT<4> { typedef uint32_t T; };
+
+template <int ESZ, int D, int MODE>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+  typedef typename ElemT<ESZ>::T E;
+  typedef Frag<ESZ, D> F;
+  extern __shared__ __align__(16) float lds[];
+
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = a.hq / a.hkv;
+  const int T = a.seq_lens[b];
+  const int P = a.page;
+  const int NP = (T + P - 1) / P;
+
+  int n_items = NP;
+  const int32_t* sel_row = nullptr;
+  if (MODE == MODE_SPARSE) {
+    const int64_t row = (int64_t)b * a.sel_rows + (a.sel_rows == 1 ? 0 : g);
+    n_items = min(max(a.sel_count[row], 0), min(a.sel_cap, NP));
+    sel_row = a.sel + row * a.sel_cap;
+  }
+  const int i0 = s * a.pps;
+  const int i1 = min(i0 + a.pps, n_items);
+  if (i0 >= i1) return;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, j = lane >> 4;
+  const bool head_ok = n < G;
+
+  typename F::QF qf[F::NL];
+  F::load_q(qf, reinterpret_cast<const E*>(a.q) + ((int64_t)b * a.hq + g * G + (head_ok ? n : 0)) * D,
+            head_ok, j);
+
+  const E* kpool = reinterpret_cast<const E*>(a.k_pool);
+  const E* vpool = reinterpret_cast<const E*>(a.v_pool);
+  const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
+  const int spp = P / kSub;
+  const int n_sub = (i1 - i0) * spp;
+  const float qk_scale2 = a.sm_scale * kLog2e;
+
+  auto resolve = [&](int u, int64_t& base, int& t0) -> bool {
+    if (u >= n_sub) return false;
+    const int it = u / spp;
+    const int sub = u - it * spp;
+    int lp = i0 + it;
+    if (MODE == MODE_SPARSE) {
+      lp = sel_row[i0 + it];
+      if (lp < 0 || lp >= NP) return false;
+    }
+    t0 = lp * P + sub * kSub;
+    if (t0 >= T) return false;
+    const int64_t phys = ptab[lp];
+    base = ((phys * a.hkv + g) * P + sub * kSub) * (int64_t)D;
+    return true;
+  };
+
+  float m2 = -INFINITY;  // running max, log2 units
+  float l = 0.f;         // this lane's share of the running sum
+  f32x4 o[F::NO];
+#pragma unroll
+  for (int x = 0; x < F::NO; ++x) o[x] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  F cur, nxt;
+  int64_t cb = 0, nb = 0;
+  int ct = 0, nt = 0;
+  int u = wave;
+  bool cv = resolve(u, cb, ct);
+  if (cv) cur.load(kpool + cb, vpool + cb, lane);
+  while (u < n_sub) {
+    const int un = u + kWaves;
+    const bool nv = resolve(un, nb, nt);
+    if (nv) nxt.load(kpool + nb, vpool + nb, lane);
+    if (cv) {
+      const f32x4 sacc = cur.qk(qf);
+      const int tb = ct + 4 * j;
+      float s2[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s2[r] = (tb + r < T) ? sacc[r] * qk_scale2 : -INFINITY;
+        mx = fmaxf(mx, s2[r]);
+      }
+      if (MODE == MODE_DELTA && head_ok) {
+        f32x4 w;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = (tb + r < T) ? sacc[r] * a.sm_scale : -INFINITY;
+        *reinterpret_cast<f32x4*>(a.logits + ((int64_t)b * a.hq + g * G + n) * a.t_pad + tb) = w;
+      }
+      mx = fmaxf(mx, shfl_xor_f(mx, 16));
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      const float m_new = fmaxf(m2, mx);
+      const float alpha = exp2f(m2 - m_new);
+      float p[4];
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = exp2f(s2[r] - m_new);
+        ps += p[r];
+      }
+      l = l * alpha + ps;
+      m2 = m_new;
+#pragma unroll
+      for (int x = 0; x < F::NO; ++x) o[x] *= alpha;
+      if (ct + kSub > T) cur.mask_v(T - ct, j);
+      cur.pv(o, p);
+    }
+    cur = nxt;
+    cv = nv;
+    cb = nb;
+    ct = nt;
+    u = un;
+  }
+
+  l += shfl_xor_f(l, 16);
+  l += shfl_xor_f(l, 32);
+
+  // merge the waves of this workgroup through LDS
+  float* lo = lds;                       // [kWaves][G][D]
+  float* lm = lds + kWaves * G * D;      // [kWaves][16]
+  float* ll = lm + kWaves * 16;          // [kWaves][16]
+  if (head_ok) {
+#pragma unroll
+    for (int x = 0; x < F::NO; ++x)
+      *reinterpret_cast<f32x4*>(lo + (wave * G + n) * D + 16 * x + 4 * j) = o[x];
+    if (j == 0) {
+      lm[wave * 16 + n] = m2;
+      ll[wave * 16 + n] = l;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    const int hn = idx / D, d = idx - hn * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lm[w * 16 + hn]);
+    float acc = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = exp2f(lm[w * 16 + hn] - M);
+        acc += f * lo[(w * G + hn) * D + d];
+        L += f * ll[w * 16 + hn];
+      }
+    }
+    const int64_t row = ((int64_t)b * a.hq + g * G + hn) * a.s_cap + s;
+    a.o_part[row * D + d] = acc;
+    if (d == 0) {
+      a.ml_part[row * 2] = M;
+      a.ml_part[row * 2 + 1] = L;
+    }
+  }
+}
+
+// One (head, sequence) per block, one head-dim element per thread.
+template <int ESZ>
+__global__ void combine_kernel(CombineArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x, D = blockDim.x;
+  const int G = a.hq / a.hkv, g = h / G;
+  const int T = a.seq_lens[b];
+  int n_items;
+  if (a.sel_count) {
+    const int64_t row = (int64_t)b * a.sel_rows + (a.sel_rows == 1 ? 0 : g);
+    n_items = min(max(a.sel_count[row], 0), min(a.sel_cap, (T + a.page - 1) / a.page));
+  } else {
+    n_items = (T + a.page - 1) / a.page;
+  }
+  const int S = min((n_items + a.pps - 1) / a.pps, a.splits);
+  const int64_t row0 = ((int64_t)b * a.hq + h) * a.s_cap;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, a.ml_part[(row0 + s) * 2]);
+  float acc = 0.f, L = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < S; ++s) {
+      const float f = exp2f(a.ml_part[(row0 + s) * 2] - M);
+      L += f * a.ml_part[(row0 + s) * 2 + 1];
+      acc += f * a.o_part[(row0 + s) * D + d];
+    }
+  }
+  const float val = (L > 0.f) ? acc / L : 0.f;
+  const int64_t oi = ((int64_t)b * a.hq + h) * D + d;
+  if (ESZ == 2)
+    reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_rne(val);
+  else
+    reinterpret_cast<float*>(a.out)[oi] = val;
+  if (d == 0) {
+    const float lse = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
+    if (a.lse) a.lse[(int64_t)b * a.hq + h] = lse;
+    if (a.lse2) a.lse2[(int64_t)b * a.hq + h] = lse;
+  }
+}
+
+template <int ESZ, int D>
+static hipError_t launch_decode_t(int mode, const DecodeArgs& a, int splits, int batch,
+                                  hipStream_t st) {
+  const int G = a.hq / a.hkv;
+  const size_t lds = (size_t)(kWaves * G * D + 2 * kWaves * 16) * sizeof(float);
+  dim3 grid(splits, a.hkv, batch);
+  if (mode == MODE_FULL)
+    hipLaunchKernelGGL((decode_kernel<ESZ, D, MODE_FULL>), grid, dim3(256), lds, st, a);
+  else if (mode == MODE_DELTA)
+    hipLaunchKernelGGL((decode_kernel<ESZ, D, MODE_DELTA>), grid, dim3(256), lds, st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<ESZ, D, MODE_SPARSE>), grid, dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(int dtype, int mode, int D, const DecodeArgs& a, int splits, int batch,
+                         hipStream_t st) {
+  if (splits == 0 || batch == 0) return hipSuccess;
+  if (dtype == 0) {
+    if (D == 128) return launch_decode_t<2, 128>(mode, a, splits, batch, st);
+    if (D == 64) return launch_decode_t<2, 64>(mode, a, splits, batch, st);
+  } else {
+    if (D == 128) return launch_decode_t<4, 128>(mode, a, splits, batch, st);
+    if (D == 64) return launch_decode_t<4, 64>(mode, a, splits, batch, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_combine(int dtype, int D, const CombineArgs& a, int batch, hipStream_t st) {
+  if (batch == 0) return hipSuccess;
+  dim3 grid(a.hq, batch);
+  if (dtype == 0)
+    hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(D), 0, st, a);
+  else
+    hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(D), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace lak

@@ -1,0 +1,72 @@
+// Device-side building blocks shared by the kernels: the in-page layout of the
+// K/V pools, MFMA fragment types and wave-level reductions (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lak {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWaves = 4;          // waves per decode workgroup
+constexpr int kSub = 16;           // tokens per sub-tile (one MFMA N/M dimension)
+
+// ---------------------------------------------------------------------------
+// In-page layout.  A page of one KV head holds P tokens as P/16 sub-tiles of
+// 16 tokens x D elements.  Inside a sub-tile the elements are ordered so that
+// the 64 lanes of a wave fetch MFMA operand fragments with one contiguous
+// 1 KiB load per instruction (16 bytes per lane, lane-ordered):
+//   K: [D/W][16 tokens][W]                   W = 16 bytes / element size
+//      -> lane l, load i: token l%16, elements d = (4i + l/16)*W .. +W
+//         (the A operand of the q.K^T MFMA: rows = tokens, k = head dim)
+//   V: [D/(16H)][4][16][H][4]                H = W / 4
+//      -> lane l, load i: d = 16(H i + h) + l%16 for h < H, tokens 4(l/16) .. +4
+//         (the A operand of the P.V MFMA: rows = head dim, k = tokens)
+// ---------------------------------------------------------------------------
+template <int ESZ>
+__host__ __device__ inline int k_off(int tt, int d) {
+  constexpr int W = 16 / ESZ;
+  return ((d / W) * kSub + tt) * W + d % W;
+}
+template <int ESZ>
+__host__ __device__ inline int v_off(int tt, int d) {
+  constexpr int H = (16 / ESZ) / 4;
+  return (((d / (16 * H)) * 4 + tt / 4) * 16 + d % 16) * (4 * H) + ((d / 16) % H) * 4 + tt % 4;
+}
+
+// Element offset of (physical page, kv head, token-in-page) sub-tile start.
+__device__ inline int64_t subtile_base(int64_t phys, int g, int t_in_page, int hkv, int P, int D) {
+  return ((phys * hkv + g) * P + (t_in_page / kSub) * kSub) * (int64_t)D;
+}
+
+// ---------------------------------------------------------------------------
+// Wave-level helpers
+// ---------------------------------------------------------------------------
+__device__ inline float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ inline int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7F800000u) == 0x7F800000u) return (uint16_t)((b >> 16) | ((b & 0xFFFF) ? 0x40 : 0));
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+__device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// Inclusive prefix sum over a wave (64 lanes).
+__device__ inline int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+}  // namespace lak

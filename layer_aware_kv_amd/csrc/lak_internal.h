@@ -1,0 +1,102 @@
+// Host-side declarations shared by the ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lak {
+
+enum Mode { MODE_FULL = 0, MODE_DELTA = 1, MODE_SPARSE = 2 };
+
+// Arguments of the split-K decode kernel (all three tiers).
+struct DecodeArgs {
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_table;   // [max_batch][max_pages]
+  const int32_t* seq_lens;     // [max_batch]
+  const void* q;               // [B][Hq][D]
+  float sm_scale;
+  int hq, hkv, page, max_pages;
+  int pps;                     // items (pages or selection entries) per split
+  int s_cap;                   // split stride of the partial buffers
+  // sparse tier
+  const int32_t* sel;          // [B][R][sel_cap]
+  const int32_t* sel_count;    // [B][R]
+  int sel_cap;
+  int sel_rows;                // R: Hkv (per KV head) or 1 (shared)
+  // outputs
+  float* o_part;               // [B][Hq][s_cap][D]
+  float* ml_part;              // [B][Hq][s_cap][2]  (max in log2 units, sum)
+  float* logits;               // delta tier: [B][Hq][t_pad]
+  int64_t t_pad;
+};
+
+struct CombineArgs {
+  const float* o_part;
+  const float* ml_part;
+  const int32_t* seq_lens;
+  const int32_t* sel_count;   // sparse tier: [B][R]; NULL for full
+  int sel_cap, sel_rows;
+  int hq, hkv, page, pps, s_cap;
+  int splits;                 // splits launched by the decode kernel
+  void* out;                  // [B][Hq][D]
+  float* lse;                 // [B][Hq] (may be NULL)
+  float* lse2;                // second copy (may be NULL)
+};
+
+struct PageScoreArgs {
+  const float* logits;        // [B][Hq][t_pad]
+  const float* lse;           // [B][Hq]
+  const int32_t* seq_lens;
+  float* scores;              // [B][R][max_pages]
+  int64_t t_pad;
+  int hq, hkv, page, max_pages;
+  int agg;                    // 0 max, 1 sum
+  int scope;                  // 0 group, 1 all
+  int tokens_per_block;
+};
+
+struct TopkArgs {
+  const float* scores;        // [B][R][max_pages]
+  const int32_t* seq_lens;
+  int32_t* sel;               // [B][R][sel_cap]
+  int32_t* sel_count;         // [B][R]
+  int rows_per_seq;           // R
+  int page, max_pages, k_top, recency, sel_cap;
+};
+
+constexpr int kStepMax = 96;
+struct StepUpdate {
+  int32_t n;          // page-table entries to write
+  int32_t batch;      // sequences whose length grows by one (0: none)
+  int32_t b[kStepMax];
+  int32_t lp[kStepMax];
+  int32_t page[kStepMax];
+};
+
+struct KvGeom {
+  int hkv, d, page, max_pages, esz;
+};
+
+// launchers (return hipSuccess or the launch error)
+hipError_t launch_decode(int dtype, int mode, int D, const DecodeArgs& a, int splits, int batch,
+                         hipStream_t st);
+hipError_t launch_combine(int dtype, int D, const CombineArgs& a, int batch, hipStream_t st);
+hipError_t launch_page_score(const PageScoreArgs& a, int batch, int rows, int max_np,
+                             hipStream_t st);
+hipError_t launch_topk(const TopkArgs& a, int batch, hipStream_t st);
+hipError_t launch_step_update(const StepUpdate& u, int32_t* page_table, int32_t* seq_lens,
+                              int max_pages, hipStream_t st);
+hipError_t launch_append(const KvGeom& g, void* kp, void* vp, const int32_t* pt,
+                         const int32_t* lens, const void* kn, const void* vn, int batch,
+                         hipStream_t st);
+hipError_t launch_prefill(const KvGeom& g, void* kp, void* vp, const int32_t* pt,
+                          const int32_t* lens, const void* k, const void* v, int64_t t_stride,
+                          int batch, int max_t, hipStream_t st);
+hipError_t launch_write_rows(const KvGeom& g, void* kp, void* vp, const int32_t* pt,
+                             const int32_t* lens, int n, const int32_t* rows, const void* kr,
+                             const void* vr, int batch, hipStream_t st);
+hipError_t launch_gather(const KvGeom& g, const void* kp, const void* vp, const int32_t* pt,
+                         int b, int gh, int t0, int n, void* ko, void* vo, hipStream_t st);
+
+}  // namespace lak

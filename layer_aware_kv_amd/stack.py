@@ -1,0 +1,74 @@
+"""Decode-step driver over a layer stack (the three-tier schedule of DELTA).
+
+"Methodology in Plain English" (DELTA AI summary page): layers 0 and 1 run full
+attention, a few delta-layers run full attention and refresh the page selection,
+every other layer runs sparse attention over the latest selection; the selection
+is recomputed for every generated token.  "Main Findings": layer 2 is always the
+first delta-layer.
+"""
+from __future__ import annotations
+
+import torch
+
+from .cache import PagedKVCache
+
+
+def layer_tiers(num_layers, full_layers, delta_layers):
+    tiers = []
+    for layer in range(num_layers):
+        if layer in full_layers:
+            tiers.append("full")
+        elif layer in delta_layers:
+            tiers.append("delta")
+        else:
+            tiers.append("sparse")
+    return tiers
+
+
+class DeltaStack:
+    """Runs decode steps of an attention-only stack on one PagedKVCache.
+
+    Per layer and step: append the step's K/V, then full / delta-select / sparse
+    attention.  Outputs of every layer are kept in ``out[l]`` / ``lse[l]``; the
+    selection installed by delta-layer l in ``sel[l]`` / ``sel_count[l]``.
+    """
+
+    def __init__(self, cache: PagedKVCache, tiers, k_top, recency, sm_scale, agg="max", scope="group"):
+        if tiers and tiers[0] == "sparse":
+            raise ValueError("a stack cannot start with a sparse layer")
+        first_delta = next((i for i, t in enumerate(tiers) if t == "delta"), None)
+        if any(t == "sparse" for t in tiers) and (first_delta is None or
+                                                  tiers.index("sparse") < first_delta):
+            raise ValueError("a sparse layer comes before any delta-layer")
+        self.c = cache
+        self.tiers = list(tiers)
+        self.k_top, self.recency, self.sm_scale = k_top, recency, sm_scale
+        self.agg, self.scope = agg, scope
+        B, L = cache.max_batch, len(tiers)
+        dev = cache.device
+        self.out = torch.zeros((L, B, cache.hq, cache.d), dtype=cache.torch_dtype, device=dev)
+        self.lse = torch.zeros((L, B, cache.hq), dtype=torch.float32, device=dev)
+        R = cache.sel_rows(scope)
+        self.sel = {l: torch.full((B, R, k_top + recency), -1, dtype=torch.int32, device=dev)
+                    for l, t in enumerate(tiers) if t == "delta"}
+        self.sel_count = {l: torch.zeros((B, R), dtype=torch.int32, device=dev)
+                          for l, t in enumerate(tiers) if t == "delta"}
+
+    def step(self, q, k_new, v_new):
+        """One decode step.  q [L][B][Hq][D]; k_new, v_new [L][B][Hkv][D] (cache dtype)."""
+        c = self.c
+        B = c.batch
+        c.step_begin()
+        cur = None
+        for layer, tier in enumerate(self.tiers):
+            c.kv_append(layer, k_new[layer], v_new[layer])
+            out, lse = self.out[layer, :B], self.lse[layer, :B]
+            if tier == "full":
+                c.attn_full(layer, q[layer], self.sm_scale, out, lse)
+            elif tier == "delta":
+                sel, cnt = self.sel[layer][:B], self.sel_count[layer][:B]
+                c.attn_delta_select(layer, q[layer], self.sm_scale, self.k_top, self.recency, self.agg, self.scope,
+                                    out, lse, sel, cnt)
+                cur = (sel, cnt)
+            else:
+                c.attn_sparse(layer, q[layer], self.sm_scale, cur[0], cur[1], self.scope, out, lse)

@@ -1,0 +1,266 @@
+"""GPU parity of every kernel through the C ABI against the CPU oracle.
+
+Sizes span several sub-tiles, splits and a ragged tail; inputs come from the seeded
+generator (workload.cases) and are exact in the stored dtype, so the oracle sees
+the same values as the device.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.delta import page_scores as o_page_scores, token_scores as o_token_scores
+from tests.gpu_util import (TOL, LSE_TOL, assert_close, check_selection, fill_and_step, host, make_cache,
+                            to_dev, tdtype)
+from workload.cases import random_case, plant_salient
+
+pytestmark = pytest.mark.gpu
+
+# id, dtype, B, Hq, Hkv, D, P, lengths
+CASES = [
+    ("f32_g4_d64_t1024", "f32", 1, 8, 2, 64, 16, [1024]),
+    ("bf16_g7_d128_t8192", "bf16", 1, 28, 4, 128, 16, [8192]),
+    ("bf16_ragged_p16", "bf16", 6, 28, 4, 128, 16, [1, 15, 16, 17, 1000, 2049]),
+    ("bf16_ragged_p32_g4", "bf16", 4, 32, 8, 128, 32, [31, 32, 33, 3000]),
+    ("bf16_g1_d64", "bf16", 2, 4, 4, 64, 16, [100, 700]),
+    ("bf16_g16_d128", "bf16", 2, 16, 1, 128, 16, [257, 1300]),
+    ("f32_g8_d128_p32", "f32", 2, 8, 1, 128, 32, [65, 999]),
+    ("bf16_p64_g4", "bf16", 2, 8, 2, 64, 64, [65, 1300]),
+]
+IDS = [c[0] for c in CASES]
+
+
+def _case(spec, seed=11):
+    name, dtype, B, HQ, HKV, D, P, lens = spec
+    scale = 1.0 / np.sqrt(D)
+    c = random_case(seed, B, HQ, HKV, D, lens, dtype)
+    G = HQ // HKV
+    for b in range(B):
+        T = lens[b]
+        if T > 64:
+            plant_salient(c, b, 0, [T // 7, T // 3, T // 2], G)
+    return c, P, float(scale)
+
+
+def _budget(T, P):
+    NP = -(-T // P)
+    return max(1, NP // 5), 2
+
+
+@pytest.mark.parametrize("spec", CASES, ids=IDS)
+def test_full_attention(spec):
+    case, P, sm = _case(spec)
+    cache = make_cache(case, P)
+    q = fill_and_step(cache, case)
+    out, lse = cache.attn_full(0, q, sm)
+    torch.cuda.synchronize()
+    for b, T in enumerate(case.lengths):
+        ref, ref_lse, _ = oracle.full_attention(case.q[b], case.K[b, :, :T], case.V[b, :, :T], sm)
+        assert_close(host(out[b]), ref, TOL[case.dtype], f"out b={b}")
+        assert_close(host(lse[b]), ref_lse, LSE_TOL[case.dtype], f"lse b={b}")
+
+
+@pytest.mark.parametrize("agg", ["max", "sum"])
+@pytest.mark.parametrize("scope", ["group", "all"])
+@pytest.mark.parametrize("spec", CASES, ids=IDS)
+def test_delta_select(spec, agg, scope):
+    case, P, sm = _case(spec)
+    cache = make_cache(case, P)
+    q = fill_and_step(cache, case)
+    T0 = case.lengths[0]
+    k_top, rec = _budget(max(case.lengths), P)
+    B = len(case.lengths)
+    R = cache.sel_rows(scope)
+    scores = torch.full((B, R, cache.max_pages), -7.0, dtype=torch.float32, device="cuda")
+    out_f, lse_f = cache.attn_full(0, q, sm)
+    out, lse, sel, cnt = cache.attn_delta_select(0, q, sm, k_top, rec, agg, scope, page_scores=scores,
+                                                 sel_capacity=k_top + rec + 3)
+    torch.cuda.synchronize()
+    # the delta-layer's attention output is the full-attention output, bit for bit
+    assert torch.equal(out, out_f) and torch.equal(lse, lse_f)
+    hkv = case.K.shape[1]
+    for b, T in enumerate(case.lengths):
+        r = oracle.delta_layer(case.q[b], case.K[b, :, :T], case.V[b, :, :T], sm, P, k_top, rec, agg, scope)
+        NP = -(-T // P)
+        S = r["page_scores"]
+        got = scores[b].cpu().numpy().astype(np.float64)
+        np.testing.assert_allclose(got[:, :NP], S, rtol=1e-4, atol=1e-7)
+        assert np.all(got[:, NP:] == -7.0)  # entries past NP untouched
+        for row in range(R):
+            check_selection(sel[b, row].cpu().numpy(), int(cnt[b, row]), S[row], k_top, rec, sel.shape[-1])
+
+
+@pytest.mark.parametrize("spec", CASES, ids=IDS)
+def test_sparse_attention(spec):
+    case, P, sm = _case(spec)
+    cache = make_cache(case, P)
+    q = fill_and_step(cache, case)
+    k_top, rec = _budget(max(case.lengths), P)
+    _, _, sel, cnt = cache.attn_delta_select(0, q, sm, k_top, rec)
+    out, lse = cache.attn_sparse(0, q, sm, sel, cnt)
+    torch.cuda.synchronize()
+    hkv = case.K.shape[1]
+    for b, T in enumerate(case.lengths):
+        sels = [sel[b, g, :int(cnt[b, g])].cpu().tolist() for g in range(hkv)]  # the GPU's own selection
+        ref, ref_lse = oracle.sparse_attention(case.q[b], case.K[b, :, :T], case.V[b, :, :T], sels, P, sm)
+        assert_close(host(out[b]), ref, TOL[case.dtype], f"sparse out b={b}")
+        assert_close(host(lse[b]), ref_lse, LSE_TOL[case.dtype], f"sparse lse b={b}")
+
+
+@pytest.mark.parametrize("spec", CASES[:4], ids=IDS[:4])
+def test_sparse_with_whole_context_equals_full(spec):
+    case, P, sm = _case(spec)
+    cache = make_cache(case, P)
+    q = fill_and_step(cache, case)
+    NPmax = -(-max(case.lengths) // P)
+    out_f, lse_f = cache.attn_full(0, q, sm)
+    # budget covering the context: every page is selected
+    _, _, sel, cnt = cache.attn_delta_select(0, q, sm, NPmax, 1)
+    out_s, lse_s = cache.attn_sparse(0, q, sm, sel, cnt)
+    torch.cuda.synchronize()
+    for b, T in enumerate(case.lengths):
+        NP = -(-T // P)
+        assert int(cnt[b, 0]) == NP and sel[b, 0, :NP].cpu().tolist() == list(range(NP))
+    assert_close(host(out_s), host(out_f), 1e-6 if case.dtype == "f32" else 8e-3, "sparse(all) vs full")
+    assert_close(host(lse_s), host(lse_f), 1e-5, "lse")
+
+
+def _tie_scores(rng, B, R, NP, levels):
+    return (rng.integers(0, levels, size=(B, R, NP)) / levels).astype(np.float32)
+
+
+@pytest.mark.parametrize("NP,k_top,rec,levels", [
+    (64, 8, 4, 5), (512, 96, 32, 3), (4100, 192, 64, 50), (1000, 0, 8, 4), (30, 40, 4, 3),
+    (7, 3, 9, 2), (2049, 2048, 0, 2), (300, 17, 0, 1000000)])
+def test_page_select_on_oracle_scores_is_exact(NP, k_top, rec, levels):
+    from layer_aware_kv_amd import PagedKVCache
+    B, R, P = 3, 2, 16
+    rng = np.random.default_rng(NP + k_top)
+    S = _tie_scores(rng, B, R, NP, levels)
+    S[0, 0, :] = 0.0  # an all-zero row
+    cache = PagedKVCache(1, B, 2 * R, R, 64, P, NP + 1, B * (NP + 1), "bf16")
+    lens = [NP * P, NP * P - 5, max(1, (NP // 2) * P)]
+    cache.seq_reset(lens)
+    dev = torch.zeros((B, R, NP + 1), dtype=torch.float32, device="cuda")
+    dev[:, :, :NP] = torch.from_numpy(S).cuda()
+    sel, cnt = cache.page_select(dev, k_top, rec)
+    torch.cuda.synchronize()
+    for b in range(B):
+        np_b = -(-lens[b] // P)
+        for r in range(R):
+            row = S[b, r, :np_b]
+            NC = max(0, np_b - rec)
+            order = sorted(range(NC), key=lambda j: (-float(row[j]), j))[:k_top]  # float32 values
+            ref = sorted(order + list(range(NC, np_b)))
+            n = int(cnt[b, r])
+            assert n == len(ref)
+            assert sel[b, r, :n].cpu().tolist() == ref
+            assert (sel[b, r, n:] == -1).all()
+
+
+@pytest.mark.parametrize("dtype,D,P", [("bf16", 128, 16), ("f32", 64, 16), ("bf16", 128, 32), ("bf16", 64, 64)])
+def test_kv_prefill_append_gather_roundtrip(dtype, D, P):
+    lens = [1, 17, 63, 200]
+    case = random_case(5, 4, 4, 2, D, lens, dtype)
+    cache = make_cache(case, P, num_layers=2, extra_tokens=40)
+    cache.seq_reset([n - 1 for n in lens], reserve_tokens=0)
+    k, v = to_dev(case.K, dtype), to_dev(case.V, dtype)
+    cache.kv_prefill(1, k, v)
+    # decode steps across page boundaries
+    extra = random_case(6, 4, 4, 2, D, [40] * 4, dtype)
+    kx, vx = to_dev(extra.K, dtype), to_dev(extra.V, dtype)
+    for s in range(40):
+        cache.step_begin()
+        if s == 0:
+            kn = torch.stack([k[b, :, lens[b] - 1] for b in range(4)]).contiguous()
+            vn = torch.stack([v[b, :, lens[b] - 1] for b in range(4)]).contiguous()
+        else:
+            kn, vn = kx[:, :, s].contiguous(), vx[:, :, s].contiguous()
+        cache.kv_append(1, kn, vn)
+    assert cache.seq_lens_host() == [n + 39 for n in lens]
+    assert cache.seq_lens.cpu().tolist()[:4] == [n + 39 for n in lens]
+    for b in range(4):
+        pt = cache.page_table_host(b)
+        assert cache.page_table[b, :len(pt)].cpu().tolist() == pt
+        for g in range(2):
+            kg, vg = cache.kv_gather(1, b, g, 0, lens[b] + 39)
+            exp_k = torch.cat([k[b, g, :lens[b]], kx[b, g, 1:40]])
+            exp_v = torch.cat([v[b, g, :lens[b]], vx[b, g, 1:40]])
+            assert torch.equal(kg, exp_k) and torch.equal(vg, exp_v)
+    # single-row overwrite
+    rows = torch.tensor([[0, 1, 0], [3, 0, 150], [2, 1, 10 ** 6]], dtype=torch.int32, device="cuda")
+    kr = torch.randn(3, D, device="cuda").to(tdtype(dtype))
+    cache.kv_write_rows(1, rows, kr)
+    kg, _ = cache.kv_gather(1, 3, 0, 150, 1)
+    assert torch.equal(kg[0], kr[1])
+    kg, _ = cache.kv_gather(1, 0, 1, 0, 1)
+    assert torch.equal(kg[0], kr[0])
+
+
+def test_edge_cases_empty_and_degenerate():
+    from layer_aware_kv_amd import PagedKVCache
+    # a sequence of length 0 (no decode step yet): out = 0, lse = -inf
+    cache = PagedKVCache(1, 2, 8, 2, 64, 16, 8, 16, "bf16")
+    cache.seq_reset([0, 20])
+    case = random_case(3, 2, 8, 2, 64, [1, 20], "bf16")
+    cache.kv_prefill(0, to_dev(case.K, "bf16"), to_dev(case.V, "bf16"))
+    q = to_dev(case.q, "bf16")
+    out, lse = cache.attn_full(0, q, 0.125)
+    _, _, sel, cnt = cache.attn_delta_select(0, q, 0.125, 1, 1)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert cnt[0].tolist() == [0, 0] and (sel[0] == -1).all()
+    ref, _, _ = oracle.full_attention(case.q[1], case.K[1, :, :20], case.V[1, :, :20], 0.125)
+    assert_close(host(out[1]), ref, 2e-2)
+    # k_top = 0 and recency = 0: an empty selection; sparse over it gives 0 / -inf
+    _, _, sel, cnt = cache.attn_delta_select(0, q, 0.125, 0, 0, sel_capacity=1)
+    out_s, lse_s = cache.attn_sparse(0, q, 0.125, sel, cnt)
+    torch.cuda.synchronize()
+    assert (cnt == 0).all() and torch.all(out_s == 0) and torch.all(torch.isneginf(lse_s))
+    # an empty batch is a no-op
+    cache.seq_reset([])
+    e = torch.empty((0, 8, 64), dtype=torch.bfloat16, device="cuda")
+    cache.attn_full(0, e, 0.125, out=e, lse=torch.empty((0, 8), device="cuda"))
+    torch.cuda.synchronize()
+
+
+def test_invalid_selection_entries_are_skipped():
+    case = random_case(9, 1, 8, 2, 64, [500], "bf16")
+    cache = make_cache(case, 16)
+    q = fill_and_step(cache, case)
+    sel = torch.tensor([[[3, -1, 31, 999, 5], [0, 1, 2, -5, 40]]], dtype=torch.int32, device="cuda")
+    cnt = torch.tensor([[5, 4]], dtype=torch.int32, device="cuda")
+    out, _ = cache.attn_sparse(0, q, 0.125, sel, cnt)
+    torch.cuda.synchronize()
+    ref, _ = oracle.sparse_attention(case.q[0], case.K[0, :, :500], case.V[0, :, :500], [[3, 31, 5], [0, 1, 2]],
+                                     16, 0.125)
+    assert_close(host(out[0]), ref, 2e-2)
+
+
+def test_errors_reported_before_launch():
+    from layer_aware_kv_amd import LakError
+    case = random_case(9, 1, 8, 2, 64, [100], "bf16")
+    cache = make_cache(case, 16)
+    q = fill_and_step(cache, case)
+    with pytest.raises(LakError, match="LAK_EINVAL"):
+        cache.attn_delta_select(0, q, 0.125, 10, 10, sel_capacity=5)
+    with pytest.raises(LakError, match="LAK_EINVAL"):
+        cache.attn_full(3, q, 0.125)
+    with pytest.raises(LakError, match="LAK_EINVAL"):
+        cache.attn_delta_select(0, q, 0.125, -1, 1)
+
+
+def test_deterministic_bitwise():
+    spec = CASES[2]
+    res = []
+    for _ in range(2):
+        case, P, sm = _case(spec)
+        cache = make_cache(case, P)
+        q = fill_and_step(cache, case)
+        scores = torch.zeros((len(case.lengths), 4, cache.max_pages), device="cuda")
+        out, lse, sel, cnt = cache.attn_delta_select(0, q, sm, 20, 3, page_scores=scores)
+        out_s, lse_s = cache.attn_sparse(0, q, sm, sel, cnt)
+        torch.cuda.synchronize()
+        res.append([t.clone() for t in (out, lse, sel, cnt, scores, out_s, lse_s)])
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
