@@ -1,0 +1,360 @@
+#!/usr/bin/env python3
+"""Decode-attention throughput of DELTA's three-tier layer stack on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+
+Workload (default): the 28-layer attention-only decode stack at long reasoning
+length -- batch 16, context 65536 tokens, 28 query / 4 KV heads, head dim 128,
+page 16, bf16; layers 0-1 full, delta-layers 2, 9, 16, 23, the other 22 layers
+sparse over a 4096-token budget (192 top-k pages + 64 recency pages).  All inputs
+(prefilled KV cache, every step's queries and appended keys/values) are generated
+on the device before timing, so they are resident in HBM.
+
+A step = one decode step of the whole stack: page-table step, KV append, and
+full / delta-select / sparse attention in every layer.  Timed: exactly K steps
+after W warm-up steps, bracketed by torch.cuda.synchronize().
+
+Printed: one JSON line.  value = B * K / elapsed (decode tokens/s of the DELTA
+stack).  Also the all-full-attention stack on the same inputs, per-tier decode
+kernel durations (HIP events recorded by the library around its decode kernel),
+the HBM roofline of the dominant kernel, and the CPU oracle's throughput on a
+bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attention tokens/s per stack + achieved HBM GB/s (full vs sparse layers)"
+PEAK_HBM_GBPS = 8000.0
+KERNEL_NAMES = {
+    "full": "lak::decode_kernel<2, 128, MODE_FULL>",
+    "delta": "lak::decode_kernel<2, 128, MODE_DELTA>",
+    "sparse": "lak::decode_kernel<2, 128, MODE_SPARSE>",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in ("layer_aware_kv_amd/csrc/decode_kernels.hip", "layer_aware_kv_amd/csrc/lak_device.h",
+                "layer_aware_kv_amd/csrc/lak_internal.h", "layer_aware_kv_amd/csrc/api.hip",
+                "layer_aware_kv_amd/build.py"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Tracer:
+    """Hands out pre-created event pairs for the decode kernels of chosen tiers."""
+
+    def __init__(self, torch, tiers, n_pairs):
+        self.tiers = set(tiers)
+        self.pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(n_pairs)]
+        for e0, e1 in self.pool:  # torch creates the HIP event at its first record
+            e0.record()
+            e1.record()
+        self.used = 0
+        self.step = 0
+        self.records = []  # (step, layer, tier, (ev0, ev1))
+
+    def pair(self, layer, tier):
+        if tier not in self.tiers or self.used >= len(self.pool):
+            return None
+        ev = self.pool[self.used]
+        self.used += 1
+        self.records.append((self.step, layer, tier, ev))
+        return ev
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1, help="batch rows in the CPU oracle sample")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1; see DESIGN.md for how the path would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from layer_aware_kv_amd import DeltaStack, PagedKVCache, layer_tiers
+    from layer_aware_kv_amd import accounting as acc
+    from layer_aware_kv_amd._lib import event_elapsed_ms
+    from workload import CONFIGS, Recipe
+    from workload.device import DeviceInputs
+
+    wl = CONFIGS[args.config]
+    W = wl.warmup if args.warmup is None else args.warmup
+    K = wl.steps if args.steps is None else args.steps
+    S = W + K
+    B, L, HQ, HKV, D, P = wl.batch, wl.num_layers, wl.hq, wl.hkv, wl.d, wl.page
+    e = 2 if wl.dtype == "bf16" else 4
+    rec = Recipe(wl)
+    dev = DeviceInputs(rec)
+    lens0 = [int(x) for x in rec.lengths0()]
+    tiers = layer_tiers(L, wl.full_layers, wl.delta_layers)
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name} ({props.multi_processor_count} CUs), workload {wl.name}, W={W} K={K}")
+
+    # ------------------------------------------------------------------ set-up
+    t_setup = time.perf_counter()
+    max_pages = math.ceil((max(lens0) + S) / P) + 1
+    num_pages = sum(math.ceil((t + S) / P) for t in lens0)
+    cache = PagedKVCache(L, B, HQ, HKV, D, P, max_pages, num_pages, wl.dtype)
+    cache.seq_reset(lens0, reserve_tokens=S)
+    tmax = max(lens0)
+
+    def prefill_all():
+        kst = torch.empty((B, HKV, tmax, D), dtype=dev.torch_dtype, device="cuda")
+        vst = torch.empty_like(kst)
+        for layer in range(L):
+            dev.fill_kv(layer, kst, vst, tmax, epoch=0)
+            cache.kv_prefill(layer, kst, vst)
+        torch.cuda.synchronize()
+        del kst, vst
+
+    prefill_all()
+    log(f"KV cache prefilled: {2 * L * cache.k_pools[0].numel() * e / 1e9:.1f} GB in pools")
+    Q = torch.empty((S, L, B, HQ, D), dtype=dev.torch_dtype, device="cuda")
+    KN = torch.empty((S, L, B, HKV, D), dtype=dev.torch_dtype, device="cuda")
+    VN = torch.empty_like(KN)
+    tq = torch.empty((S, B, HQ, D), dtype=dev.torch_dtype, device="cuda")
+    tk = torch.empty((S, B, HKV, D), dtype=dev.torch_dtype, device="cuda")
+    tv = torch.empty_like(tk)
+    for layer in range(L):
+        dev.fill_queries(layer, 0, S, tq)
+        Q[:, layer] = tq
+        dev.fill_new_kv(layer, 0, S, tk, tv)
+        KN[:, layer] = tk
+        VN[:, layer] = tv
+    drift = {}
+    if wl.drift_every:
+        for s in range(wl.drift_every, S, wl.drift_every):
+            drift[s] = [dev.drift_rows(layer, s // wl.drift_every) for layer in range(L)]
+    torch.cuda.synchronize()
+    del tq, tk, tv
+    log(f"set-up {time.perf_counter() - t_setup:.1f} s; drift events at steps {sorted(drift)}")
+
+    state = {"dirty": False}
+
+    def run(run_tiers, tracer=None):
+        if state["dirty"]:
+            prefill_all()
+        cache.seq_reset(lens0, reserve_tokens=S)
+        stack = DeltaStack(cache, run_tiers, wl.k_top, wl.recency, wl.sm_scale)
+
+        def one(s, tr):
+            if s in drift:
+                for layer, (rows, krows) in enumerate(drift[s]):
+                    if rows is not None:
+                        cache.kv_write_rows(layer, rows, krows)
+                state["dirty"] = True
+            if tr is not None:
+                tr.step = s
+            stack.step(Q[s], KN[s], VN[s], tr)
+
+        for s in range(W):
+            one(s, None)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(W, S):
+            one(s, tracer)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    # decode-kernel bytes of one launch at step s
+    def kernel_bytes(tier, s):
+        lens = [t + s + 1 for t in lens0]
+        q_bytes = B * HQ * D * e
+        if tier == "sparse":
+            toks = sum(acc.selected_tokens(t, P, wl.k_top, wl.recency) for t in lens)
+            return toks * HKV * D * 2 * e + q_bytes + B * HKV * (wl.k_top + wl.recency) * 4
+        return sum(lens) * HKV * D * 2 * e + q_bytes
+
+    step_bytes = acc.stack_bytes([t + W + K // 2 + 1 for t in lens0], tiers, HQ, HKV, D, e, P, wl.k_top,
+                                 wl.recency)
+    present = sorted(set(tiers))
+    dom = max(present, key=lambda t: step_bytes[t])
+
+    # A: the timed DELTA stack, events around the dominant tier's decode kernel
+    trA = Tracer(torch, [dom], K * tiers.count(dom))
+    tA = run(tiers, trA)
+    value = B * K / tA
+    log(f"DELTA stack: {tA / K * 1e3:.3f} ms/step, {value:.0f} tok/s")
+
+    def summarize(records):
+        out = {}
+        for s, layer, tier, (e0, e1) in records:
+            d = out.setdefault(tier, {"launches": 0, "ms": 0.0, "bytes": 0})
+            d["launches"] += 1
+            d["ms"] += event_elapsed_ms(e0, e1)
+            d["bytes"] += kernel_bytes(tier, s)
+        for tier, d in out.items():
+            d["us_per_launch"] = 1e3 * d["ms"] / d["launches"]
+            d["achieved_GBps"] = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+            d["bytes_per_launch"] = d["bytes"] / d["launches"]
+            d["frac_of_peak"] = d["achieved_GBps"] / PEAK_HBM_GBPS
+        return out
+
+    domA = summarize(trA.records)[dom]
+
+    # B: per-tier breakdown (events around every decode kernel)
+    trB = Tracer(torch, present, K * L)
+    tB = run(tiers, trB)
+    per_tier = summarize(trB.records)
+    for t, d in per_tier.items():
+        d["ms_per_step"] = d["ms"] / K
+    log("tiers: " + ", ".join(f"{t} {d['us_per_launch']:.1f} us {d['achieved_GBps']:.0f} GB/s"
+                              for t, d in sorted(per_tier.items())))
+
+    # C: the same stack with every layer full, same inputs
+    tC = run(["full"] * L)
+    full_value = B * K / tC
+    log(f"all-full stack: {tC / K * 1e3:.3f} ms/step, {full_value:.0f} tok/s")
+
+    attended_delta = acc.attended_tokens([t + W + K // 2 + 1 for t in lens0], tiers, P, wl.k_top, wl.recency)
+    attended_full = acc.attended_tokens([t + W + K // 2 + 1 for t in lens0], ["full"] * L, P, wl.k_top,
+                                        wl.recency)
+    total_step_bytes = sum(step_bytes.values())
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            with open(TRAFFIC_FILE) as f:
+                tj = json.load(f)
+            ent = tj.get("kernels", {}).get(dom)
+            if tj.get("source_hash") == kernel_source_hash() and tj.get("workload") == wl.name and ent:
+                traffic = ent["hbm_bytes_per_launch"]
+        except (OSError, ValueError, KeyError):
+            traffic = None
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(tA / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded Philox inputs generated on the device; no datasets or weights)",
+        "config": {
+            "workload": wl.name,
+            "layers": L, "batch": B, "context": wl.context, "q_heads": HQ, "kv_heads": HKV, "head_dim": D,
+            "page": P, "top_k_pages": wl.k_top, "recency_pages": wl.recency,
+            "full_layers": list(wl.full_layers), "delta_layers": list(wl.delta_layers),
+            "ragged_min": wl.ragged_min, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": KERNEL_NAMES[dom],
+            "achieved": round(domA["achieved_GBps"], 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(domA["achieved_GBps"] / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": int(domA["bytes_per_launch"]),
+            "us_per_launch": round(domA["us_per_launch"], 2),
+            "launches": domA["launches"],
+        },
+        "tiers": {t: {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+                  for t, d in per_tier.items()},
+        "all_full_tokens_per_s": round(full_value, 2),
+        "all_full_ms_per_step": round(tC / K * 1e3, 4),
+        "speedup_vs_all_full": round(value / full_value, 4),
+        "attended_token_ratio": round(attended_full / attended_delta, 4),
+        "algorithmic_bytes_per_step": {t: int(v) for t, v in step_bytes.items()},
+        "stack_GBps": round(total_step_bytes / (tA / K) / 1e9, 1),
+        "device": props.name,
+    }
+    del cache, Q, KN, VN
+    torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, rec, tiers, W, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, rec, tiers, step, rows, repeats=3):
+    """The CPU oracle, as it stands, on a bounded sample: one decode step of ``rows``
+    batch rows through one layer of each tier, extrapolated to the stack's tier counts."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    first = {t: tiers.index(t) for t in ("full", "delta", "sparse") if t in tiers}
+    count = {t: tiers.count(t) for t in first}
+    times = {t: [] for t in first}
+    epoch = rec.epoch_of_step(step)
+    log(f"cpu baseline: {rows} row(s), layers {first}, {cores} cores")
+    with threadpool_limits(limits=cores):
+        for b in range(rows):
+            T = int(rec.lengths0()[b]) + step + 1
+            data = {}
+            for t, layer in first.items():
+                src = layer if t != "sparse" else first.get("delta", layer)
+                K, V = rec.layer_kv(layer, b, T, epoch)
+                data[t] = (rec.q(layer, step, b), K, V, src)
+            for _ in range(repeats):
+                sel = None
+                if "full" in first:
+                    q, K, V, _ = data["full"]
+                    t0 = time.perf_counter()
+                    oracle.full_attention(q, K, V, wl.sm_scale)
+                    times["full"].append(time.perf_counter() - t0)
+                if "delta" in first:
+                    q, K, V, _ = data["delta"]
+                    t0 = time.perf_counter()
+                    r = oracle.delta_layer(q, K, V, wl.sm_scale, wl.page, wl.k_top, wl.recency)
+                    times["delta"].append(time.perf_counter() - t0)
+                    sel = r["sel"]
+                if "sparse" in first:
+                    q, K, V, _ = data["sparse"]
+                    t0 = time.perf_counter()
+                    oracle.sparse_attention(q, K, V, sel, wl.page, wl.sm_scale)
+                    times["sparse"].append(time.perf_counter() - t0)
+            del data
+    per_row_step = sum(count[t] * float(np.median(times[t])) for t in first)
+    return {
+        "value": round(1.0 / per_row_step, 4),
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"one decode step (step {step}) of batch row(s) 0..{rows - 1} at full context through one "
+                   f"layer of each tier (layers {first}), median of {repeats} runs; seconds per row-step = sum over tiers of "
+                   f"(layers in tier) x (measured time); tokens/s = 1 / that (rows are independent)"),
+        "seconds_per_layer": {t: round(float(np.median(v)), 4) for t, v in times.items()},
+        "repeats": repeats,
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+if __name__ == "__main__":
+    main()

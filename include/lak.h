@@ -64,7 +64,7 @@ typedef enum { LAK_SCOPE_GROUP = 0, LAK_SCOPE_ALL = 1 } lak_scope;
 typedef struct lak_cache lak_cache; /* opaque; owns host metadata only */
 
 /* Paged KV cache description.  Supported: head_dim 64 or 128; G = Hq / Hkv in
- * 1..16; page_size a multiple of 16 up to 256.
+ * 1..16; page_size 16, 32 or 64.
  * Pools: one K and one V pool per layer, each num_pages pages of
  * [Hkv][P][D] elements (lak_pool_bytes() bytes); the in-page order of elements is
  * private to the library (written only by lak_kv_* calls).  page_table is
@@ -191,6 +191,12 @@ lak_status lak_attn_sparse(lak_cache* cache, int32_t layer, const void* q, float
                            const int32_t* sel, const int32_t* sel_count, int32_t sel_capacity,
                            int32_t scope, void* out, float* lse, void* ws, size_t ws_bytes,
                            void* stream);
+
+/* Tracing: while set, every attention call on `cache` records `before` and `after`
+ * (hipEvent_t created by the caller) on its stream immediately before and after
+ * its split-K decode kernel, so hipEventElapsedTime gives that kernel's duration.
+ * NULL, NULL stops it.  Errors: EINVAL if exactly one event is NULL. */
+lak_status lak_trace_decode(lak_cache* cache, void* before, void* after);
 
 /* Reason for the last failing call of this thread ("" if none). */
 const char* lak_last_error(void);

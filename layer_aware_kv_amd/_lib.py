@@ -58,6 +58,7 @@ SIGNATURES = {
                                    C.c_size_t, _P]),
     "lak_page_select": (_S, [_P, _P, _I32, _I32, _I32, _P, _P, _I32, _P]),
     "lak_attn_sparse": (_S, [_P, _I32, _P, _F, _P, _P, _I32, _I32, _P, _P, _P, C.c_size_t, _P]),
+    "lak_trace_decode": (_S, [_P, _P, _P]),
     "lak_last_error": (C.c_char_p, []),
 }
 
@@ -77,6 +78,24 @@ def lib():
             fn.argtypes = args
         _lib = L
     return _lib
+
+
+_hip = None
+
+
+def event_elapsed_ms(before, after) -> float:
+    """hipEventElapsedTime of two completed events (torch.cuda.Event objects recorded
+    by the library, which torch itself does not know were recorded)."""
+    global _hip
+    if _hip is None:
+        _hip = C.CDLL("libamdhip64.so")
+        _hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        _hip.hipEventElapsedTime.restype = C.c_int
+    ms = C.c_float()
+    rc = _hip.hipEventElapsedTime(C.byref(ms), C.c_void_p(before.cuda_event), C.c_void_p(after.cuda_event))
+    if rc != 0:
+        raise RuntimeError(f"hipEventElapsedTime failed with hipError {rc}")
+    return ms.value
 
 
 def check(status: int, where: str):

@@ -100,6 +100,16 @@ class PagedKVCache:
     def free_pages(self):
         return L.lib().lak_free_pages(self._h)
 
+    def trace_decode(self, before=None, after=None):
+        """Record torch.cuda.Event ``before`` / ``after`` around the decode kernel of
+        the following attention calls (None, None stops).  The events must already
+        exist on the device (torch creates one at its first ``record()``)."""
+        if before is not None and (before.cuda_event == 0 or after.cuda_event == 0):
+            raise ValueError("trace events not created yet: record() each once first")
+        b = None if before is None else C.c_void_p(before.cuda_event)
+        a = None if after is None else C.c_void_p(after.cuda_event)
+        L.check(L.lib().lak_trace_decode(self._h, b, a), "lak_trace_decode")
+
     # ------------------------------------------------------------ KV writes
     def kv_append(self, layer, k_new, v_new):
         L.check(L.lib().lak_kv_append(self._h, layer, _ptr(k_new), _ptr(v_new), _stream()), "lak_kv_append")

@@ -57,6 +57,7 @@ struct lak_cache {
   std::vector<int32_t> table_staging;
   std::vector<int32_t> lens_staging;
   int s_cap = 0;
+  hipEvent_t trace_before = nullptr, trace_after = nullptr;
 
   int max_np() const {
     int m = 0;
@@ -179,7 +180,10 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, float
   a.ml_part = reinterpret_cast<float*>(wsb + w.ml_part);
   a.logits = reinterpret_cast<float*>(wsb + w.logits);
   a.t_pad = (int64_t)d.max_pages_per_seq * d.page_size;
-  hipError_t e = launch_decode(d.dtype, mode, d.head_dim, a, splits, c->batch, st);
+  hipError_t e = hipSuccess;
+  if (c->trace_before) e = hipEventRecord(c->trace_before, st);
+  if (e == hipSuccess) e = launch_decode(d.dtype, mode, d.head_dim, a, splits, c->batch, st);
+  if (e == hipSuccess && c->trace_after) e = hipEventRecord(c->trace_after, st);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
 
   CombineArgs cb;
@@ -535,6 +539,14 @@ lak_status lak_attn_sparse(lak_cache* c, int32_t layer, const void* q, float sm_
   const int sel_rows = scope == LAK_SCOPE_GROUP ? c->d.num_kv_heads : 1;
   return run_attention(c, layer, MODE_SPARSE, q, sm_scale, out, lse, sel, sel_count, sel_capacity, sel_rows, ws,
                        static_cast<hipStream_t>(stream));
+}
+
+lak_status lak_trace_decode(lak_cache* c, void* before, void* after) {
+  if (!c) return fail(LAK_EINVAL, "cache is NULL");
+  if ((before == nullptr) != (after == nullptr)) return fail(LAK_EINVAL, "set both trace events or neither");
+  c->trace_before = static_cast<hipEvent_t>(before);
+  c->trace_after = static_cast<hipEvent_t>(after);
+  return ok();
 }
 
 const char* lak_last_error(void) { return g_err.c_str(); }

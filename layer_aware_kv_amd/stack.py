@@ -54,8 +54,12 @@ class DeltaStack:
         self.sel_count = {l: torch.zeros((B, R), dtype=torch.int32, device=dev)
                           for l, t in enumerate(tiers) if t == "delta"}
 
-    def step(self, q, k_new, v_new):
-        """One decode step.  q [L][B][Hq][D]; k_new, v_new [L][B][Hkv][D] (cache dtype)."""
+    def step(self, q, k_new, v_new, tracer=None):
+        """One decode step.  q [L][B][Hq][D]; k_new, v_new [L][B][Hkv][D] (cache dtype).
+
+        ``tracer`` (optional) has ``pair(layer, tier)`` returning a (before, after)
+        torch.cuda.Event pair to record around that layer's decode kernel, or None.
+        """
         c = self.c
         B = c.batch
         c.step_begin()
@@ -63,6 +67,9 @@ class DeltaStack:
         for layer, tier in enumerate(self.tiers):
             c.kv_append(layer, k_new[layer], v_new[layer])
             out, lse = self.out[layer, :B], self.lse[layer, :B]
+            ev = tracer.pair(layer, tier) if tracer is not None else None
+            if ev is not None:
+                c.trace_decode(*ev)
             if tier == "full":
                 c.attn_full(layer, q[layer], self.sm_scale, out, lse)
             elif tier == "delta":
@@ -72,3 +79,5 @@ class DeltaStack:
                 cur = (sel, cnt)
             else:
                 c.attn_sparse(layer, q[layer], self.sm_scale, cur[0], cur[1], self.scope, out, lse)
+            if ev is not None:
+                c.trace_decode()
