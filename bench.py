@@ -82,6 +82,93 @@ class Tracer:
         return ev
 
 
+class StackBench:
+    """Device set-up and the step loop of one stack workload (inputs resident in HBM)."""
+
+    def __init__(self, wl, warmup, steps):
+        import torch
+        from layer_aware_kv_amd import PagedKVCache, layer_tiers
+        from workload import Recipe
+        from workload.device import DeviceInputs
+
+        self.torch = torch
+        self.wl = wl
+        self.W, self.K = warmup, steps
+        self.S = warmup + steps
+        self.rec = Recipe(wl)
+        self.dev = DeviceInputs(self.rec)
+        self.lens0 = [int(x) for x in self.rec.lengths0()]
+        self.tiers = layer_tiers(wl.num_layers, wl.full_layers, wl.delta_layers)
+        B, L, P = wl.batch, wl.num_layers, wl.page
+        max_pages = math.ceil((max(self.lens0) + self.S) / P) + 1
+        num_pages = sum(math.ceil((t + self.S) / P) for t in self.lens0)
+        self.cache = PagedKVCache(L, B, wl.hq, wl.hkv, wl.d, P, max_pages, num_pages, wl.dtype)
+        self.cache.seq_reset(self.lens0, reserve_tokens=self.S)
+        self.dirty = False
+        self.prefill_all()
+        td = self.dev.torch_dtype
+        S = self.S
+        self.Q = torch.empty((S, L, B, wl.hq, wl.d), dtype=td, device="cuda")
+        self.KN = torch.empty((S, L, B, wl.hkv, wl.d), dtype=td, device="cuda")
+        self.VN = torch.empty_like(self.KN)
+        tq = torch.empty((S, B, wl.hq, wl.d), dtype=td, device="cuda")
+        tk = torch.empty((S, B, wl.hkv, wl.d), dtype=td, device="cuda")
+        tv = torch.empty_like(tk)
+        for layer in range(L):
+            self.dev.fill_queries(layer, 0, S, tq)
+            self.Q[:, layer] = tq
+            self.dev.fill_new_kv(layer, 0, S, tk, tv)
+            self.KN[:, layer] = tk
+            self.VN[:, layer] = tv
+        self.drift = {}
+        if wl.drift_every:
+            for s in range(wl.drift_every, S, wl.drift_every):
+                self.drift[s] = [self.dev.drift_rows(layer, s // wl.drift_every) for layer in range(L)]
+        torch.cuda.synchronize()
+
+    def prefill_all(self):
+        torch, wl = self.torch, self.wl
+        tmax = max(self.lens0)
+        kst = torch.empty((wl.batch, wl.hkv, tmax, wl.d), dtype=self.dev.torch_dtype, device="cuda")
+        vst = torch.empty_like(kst)
+        for layer in range(wl.num_layers):
+            self.dev.fill_kv(layer, kst, vst, tmax, epoch=0)
+            self.cache.kv_prefill(layer, kst, vst)
+        torch.cuda.synchronize()
+        self.dirty = False
+
+    def run(self, tiers, tracer=None, on_step=None):
+        """W untimed steps, then K timed steps; returns the timed seconds.  ``on_step(s,
+        stack)`` (tests only) runs after every step and is not meant for timing."""
+        from layer_aware_kv_amd import DeltaStack
+        torch, wl, cache = self.torch, self.wl, self.cache
+        if self.dirty:
+            self.prefill_all()
+        cache.seq_reset(self.lens0, reserve_tokens=self.S)
+        stack = DeltaStack(cache, tiers, wl.k_top, wl.recency, wl.sm_scale)
+
+        def one(s, tr):
+            if s in self.drift:
+                for layer, (rows, krows) in enumerate(self.drift[s]):
+                    if rows is not None:
+                        cache.kv_write_rows(layer, rows, krows)
+                self.dirty = True
+            if tr is not None:
+                tr.step = s
+            stack.step(self.Q[s], self.KN[s], self.VN[s], tr)
+            if on_step is not None:
+                on_step(s, stack)
+
+        for s in range(self.W):
+            one(s, None)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(self.W, self.S):
+            one(s, tracer)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,91 +185,24 @@ def main():
         sys.exit(2)
 
     import torch
-    from layer_aware_kv_amd import DeltaStack, PagedKVCache, layer_tiers
     from layer_aware_kv_amd import accounting as acc
     from layer_aware_kv_amd._lib import event_elapsed_ms
-    from workload import CONFIGS, Recipe
-    from workload.device import DeviceInputs
+    from workload import CONFIGS
 
     wl = CONFIGS[args.config]
     W = wl.warmup if args.warmup is None else args.warmup
     K = wl.steps if args.steps is None else args.steps
-    S = W + K
     B, L, HQ, HKV, D, P = wl.batch, wl.num_layers, wl.hq, wl.hkv, wl.d, wl.page
     e = 2 if wl.dtype == "bf16" else 4
-    rec = Recipe(wl)
-    dev = DeviceInputs(rec)
-    lens0 = [int(x) for x in rec.lengths0()]
-    tiers = layer_tiers(L, wl.full_layers, wl.delta_layers)
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name} ({props.multi_processor_count} CUs), workload {wl.name}, W={W} K={K}")
 
-    # ------------------------------------------------------------------ set-up
     t_setup = time.perf_counter()
-    max_pages = math.ceil((max(lens0) + S) / P) + 1
-    num_pages = sum(math.ceil((t + S) / P) for t in lens0)
-    cache = PagedKVCache(L, B, HQ, HKV, D, P, max_pages, num_pages, wl.dtype)
-    cache.seq_reset(lens0, reserve_tokens=S)
-    tmax = max(lens0)
-
-    def prefill_all():
-        kst = torch.empty((B, HKV, tmax, D), dtype=dev.torch_dtype, device="cuda")
-        vst = torch.empty_like(kst)
-        for layer in range(L):
-            dev.fill_kv(layer, kst, vst, tmax, epoch=0)
-            cache.kv_prefill(layer, kst, vst)
-        torch.cuda.synchronize()
-        del kst, vst
-
-    prefill_all()
-    log(f"KV cache prefilled: {2 * L * cache.k_pools[0].numel() * e / 1e9:.1f} GB in pools")
-    Q = torch.empty((S, L, B, HQ, D), dtype=dev.torch_dtype, device="cuda")
-    KN = torch.empty((S, L, B, HKV, D), dtype=dev.torch_dtype, device="cuda")
-    VN = torch.empty_like(KN)
-    tq = torch.empty((S, B, HQ, D), dtype=dev.torch_dtype, device="cuda")
-    tk = torch.empty((S, B, HKV, D), dtype=dev.torch_dtype, device="cuda")
-    tv = torch.empty_like(tk)
-    for layer in range(L):
-        dev.fill_queries(layer, 0, S, tq)
-        Q[:, layer] = tq
-        dev.fill_new_kv(layer, 0, S, tk, tv)
-        KN[:, layer] = tk
-        VN[:, layer] = tv
-    drift = {}
-    if wl.drift_every:
-        for s in range(wl.drift_every, S, wl.drift_every):
-            drift[s] = [dev.drift_rows(layer, s // wl.drift_every) for layer in range(L)]
-    torch.cuda.synchronize()
-    del tq, tk, tv
-    log(f"set-up {time.perf_counter() - t_setup:.1f} s; drift events at steps {sorted(drift)}")
-
-    state = {"dirty": False}
-
-    def run(run_tiers, tracer=None):
-        if state["dirty"]:
-            prefill_all()
-        cache.seq_reset(lens0, reserve_tokens=S)
-        stack = DeltaStack(cache, run_tiers, wl.k_top, wl.recency, wl.sm_scale)
-
-        def one(s, tr):
-            if s in drift:
-                for layer, (rows, krows) in enumerate(drift[s]):
-                    if rows is not None:
-                        cache.kv_write_rows(layer, rows, krows)
-                state["dirty"] = True
-            if tr is not None:
-                tr.step = s
-            stack.step(Q[s], KN[s], VN[s], tr)
-
-        for s in range(W):
-            one(s, None)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for s in range(W, S):
-            one(s, tracer)
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0
+    sb = StackBench(wl, W, K)
+    lens0, tiers, rec = sb.lens0, sb.tiers, sb.rec
+    log(f"set-up {time.perf_counter() - t_setup:.1f} s: {2 * L * sb.cache.k_pools[0].numel() * e / 1e9:.1f} GB "
+        f"of KV pools; drift events at steps {sorted(sb.drift)}")
 
     # decode-kernel bytes of one launch at step s
     def kernel_bytes(tier, s):
@@ -193,14 +213,14 @@ def main():
             return toks * HKV * D * 2 * e + q_bytes + B * HKV * (wl.k_top + wl.recency) * 4
         return sum(lens) * HKV * D * 2 * e + q_bytes
 
-    step_bytes = acc.stack_bytes([t + W + K // 2 + 1 for t in lens0], tiers, HQ, HKV, D, e, P, wl.k_top,
-                                 wl.recency)
+    mid = [t + W + K // 2 + 1 for t in lens0]
+    step_bytes = acc.stack_bytes(mid, tiers, HQ, HKV, D, e, P, wl.k_top, wl.recency)
     present = sorted(set(tiers))
     dom = max(present, key=lambda t: step_bytes[t])
 
     # A: the timed DELTA stack, events around the dominant tier's decode kernel
     trA = Tracer(torch, [dom], K * tiers.count(dom))
-    tA = run(tiers, trA)
+    tA = sb.run(tiers, trA)
     value = B * K / tA
     log(f"DELTA stack: {tA / K * 1e3:.3f} ms/step, {value:.0f} tok/s")
 
@@ -222,7 +242,7 @@ def main():
 
     # B: per-tier breakdown (events around every decode kernel)
     trB = Tracer(torch, present, K * L)
-    tB = run(tiers, trB)
+    sb.run(tiers, trB)
     per_tier = summarize(trB.records)
     for t, d in per_tier.items():
         d["ms_per_step"] = d["ms"] / K
@@ -230,13 +250,12 @@ def main():
                               for t, d in sorted(per_tier.items())))
 
     # C: the same stack with every layer full, same inputs
-    tC = run(["full"] * L)
+    tC = sb.run(["full"] * L)
     full_value = B * K / tC
     log(f"all-full stack: {tC / K * 1e3:.3f} ms/step, {full_value:.0f} tok/s")
 
-    attended_delta = acc.attended_tokens([t + W + K // 2 + 1 for t in lens0], tiers, P, wl.k_top, wl.recency)
-    attended_full = acc.attended_tokens([t + W + K // 2 + 1 for t in lens0], ["full"] * L, P, wl.k_top,
-                                        wl.recency)
+    attended_delta = acc.attended_tokens(mid, tiers, P, wl.k_top, wl.recency)
+    attended_full = acc.attended_tokens(mid, ["full"] * L, P, wl.k_top, wl.recency)
     total_step_bytes = sum(step_bytes.values())
 
     traffic = None
@@ -292,7 +311,7 @@ def main():
         "stack_GBps": round(total_step_bytes / (tA / K) / 1e9, 1),
         "device": props.name,
     }
-    del cache, Q, KN, VN
+    del sb
     torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

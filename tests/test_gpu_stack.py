@@ -1,0 +1,82 @@
+"""GPU parity of whole decode stacks at the workloads' full sizes, run by bench.py's
+own StackBench (the launch configuration the benchmark times).  Sampled batch
+rows, layers and steps are recomputed by the oracle from the host recipe."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import TOL, LSE_TOL, assert_close, check_selection
+from workload import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+SAMPLES = {
+    # workload: timed/warm-up steps, steps checked, batch rows, layers checked
+    2: dict(warmup=0, steps=256, check=[0, 100, 255], rows=[0, 7], layers=[0, 2, 3, 23, 27]),
+    3: dict(warmup=4, steps=2, check=[4], rows=[0, 15], layers=[0, 2, 3, 23, 27]),
+    4: dict(warmup=4, steps=2, check=[5], rows=None, layers=[0, 2, 3, 34, 35]),
+}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("index", [2, 3, 4])
+def test_stack_full_size_sampled(index):
+    import bench
+    wl = CONFIGS[index]
+    spec = SAMPLES[index]
+    print(f"stack parity: {wl.name}", flush=True)
+    sb = bench.StackBench(wl, spec["warmup"], spec["steps"])
+    rec, tiers, lens0 = sb.rec, sb.tiers, sb.lens0
+    rows = spec["rows"] or [int(np.argmin(lens0)), int(np.argmax(lens0))]
+    deltas = [l for l, t in enumerate(tiers) if t == "delta"]
+    captured = {}
+
+    def on_step(s, stack):
+        if s not in spec["check"]:
+            return
+        torch.cuda.synchronize()
+        cap = {"out": {}, "lse": {}, "sel": {}, "cnt": {}}
+        for layer in spec["layers"]:
+            cap["out"][layer] = stack.out[layer, rows].float().cpu().numpy().astype(np.float64)
+            cap["lse"][layer] = stack.lse[layer, rows].cpu().numpy().astype(np.float64)
+        for layer in deltas:
+            cap["sel"][layer] = stack.sel[layer][rows].cpu().numpy()
+            cap["cnt"][layer] = stack.sel_count[layer][rows].cpu().numpy()
+        captured[s] = cap
+
+    sb.run(tiers, on_step=on_step)
+    del sb
+    gc.collect()
+    torch.cuda.empty_cache()
+    assert sorted(captured) == spec["check"]
+
+    n_band = 0
+    for s, cap in captured.items():
+        epoch = rec.epoch_of_step(s)
+        for i, b in enumerate(rows):
+            T = lens0[b] + s + 1
+            for layer in spec["layers"]:
+                tier = tiers[layer]
+                K, V = rec.layer_kv(layer, b, T, epoch)
+                q = rec.q(layer, s, b)
+                got, got_lse = cap["out"][layer][i], cap["lse"][layer][i]
+                what = f"{wl.name} step {s} row {b} layer {layer} ({tier})"
+                if tier == "full":
+                    ref, ref_lse, _ = oracle.full_attention(q, K, V, wl.sm_scale)
+                elif tier == "delta":
+                    r = oracle.delta_layer(q, K, V, wl.sm_scale, wl.page, wl.k_top, wl.recency)
+                    ref, ref_lse = r["out"], r["lse"]
+                    for g in range(wl.hkv):
+                        n_band += check_selection(cap["sel"][layer][i, g], int(cap["cnt"][layer][i, g]),
+                                                  r["page_scores"][g], wl.k_top, wl.recency, wl.k_top + wl.recency)
+                else:
+                    src = max(d for d in deltas if d < layer)
+                    sels = [cap["sel"][src][i, g, :int(cap["cnt"][src][i, g])].tolist() for g in range(wl.hkv)]
+                    ref, ref_lse = oracle.sparse_attention(q, K, V, sels, wl.page, wl.sm_scale)
+                assert_close(got, ref, TOL[wl.dtype], what)
+                assert_close(got_lse, ref_lse, LSE_TOL[wl.dtype], what + " lse")
+                del K, V
+    print(f"{wl.name}: {n_band} selected pages differ inside the boundary band", flush=True)
