@@ -154,9 +154,14 @@ lak_status lak_kv_gather(lak_cache* cache, int32_t layer, int32_t b, int32_t g, 
 /* Full decode attention of layer `layer` (layers 0-1 and delta-layers: "run
  * ordinary full attention"): out[b][h] = sum_t p_t v_t over t < T_b with
  * p = softmax(sm_scale * <q[b][h], k_t>).  Split-K over pages plus a combine kernel.
+ * k_new, v_new (both NULL, or both device [B][Hkv][D]): this step's key and value;
+ * when given, the call also appends them at position T_b - 1, exactly as
+ * lak_kv_append would before the call (one launch fewer).  The same holds for the
+ * k_new / v_new arguments of lak_attn_delta_select and lak_attn_sparse.
  * lse may be NULL.  ws: lak_workspace_bytes() bytes of device memory. */
-lak_status lak_attn_full(lak_cache* cache, int32_t layer, const void* q, float sm_scale, void* out,
-                         float* lse, void* ws, size_t ws_bytes, void* stream);
+lak_status lak_attn_full(lak_cache* cache, int32_t layer, const void* q, const void* k_new,
+                         const void* v_new, float sm_scale, void* out, float* lse, void* ws,
+                         size_t ws_bytes, void* stream);
 
 /* Delta-layer: the full attention of lak_attn_full (same out / lse), plus the page
  * selection it installs.  Per token t < T_b: a_t = AGG over the scope's heads of
@@ -168,8 +173,9 @@ lak_status lak_attn_full(lak_cache* cache, int32_t layer, const void* q, float s
  * sel: device int32 [B][R][sel_capacity], R = Hkv (GROUP) or 1 (ALL),
  * sel_capacity >= k_top + recency.  page_scores (nullable): device float32
  * [B][R][max_pages_per_seq], entries j >= NP_b left untouched. */
-lak_status lak_attn_delta_select(lak_cache* cache, int32_t layer, const void* q, float sm_scale,
-                                 void* out, float* lse, int32_t k_top, int32_t recency,
+lak_status lak_attn_delta_select(lak_cache* cache, int32_t layer, const void* q, const void* k_new,
+                                 const void* v_new, float sm_scale, void* out, float* lse,
+                                 int32_t k_top, int32_t recency,
                                  int32_t agg, int32_t scope, int32_t* sel, int32_t* sel_count,
                                  int32_t sel_capacity, float* page_scores, void* ws,
                                  size_t ws_bytes, void* stream);
@@ -187,10 +193,10 @@ lak_status lak_page_select(lak_cache* cache, const float* page_scores, int32_t s
  * lak_attn_delta_select with the same scope; entries outside [0, NP_b) are
  * skipped; duplicates are the caller's error).  The softmax is over those tokens
  * only.  A row with no valid page yields out = 0 and lse = -inf. */
-lak_status lak_attn_sparse(lak_cache* cache, int32_t layer, const void* q, float sm_scale,
-                           const int32_t* sel, const int32_t* sel_count, int32_t sel_capacity,
-                           int32_t scope, void* out, float* lse, void* ws, size_t ws_bytes,
-                           void* stream);
+lak_status lak_attn_sparse(lak_cache* cache, int32_t layer, const void* q, const void* k_new,
+                           const void* v_new, float sm_scale, const int32_t* sel,
+                           const int32_t* sel_count, int32_t sel_capacity, int32_t scope, void* out,
+                           float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* Tracing: while set, every attention call on `cache` records `before` and `after`
  * (hipEvent_t created by the caller) on its stream immediately before and after

@@ -53,11 +53,11 @@ SIGNATURES = {
     "lak_kv_prefill": (_S, [_P, _I32, _P, _P, _I64, _P]),
     "lak_kv_write_rows": (_S, [_P, _I32, _I32, _P, _P, _P, _P]),
     "lak_kv_gather": (_S, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
-    "lak_attn_full": (_S, [_P, _I32, _P, _F, _P, _P, _P, C.c_size_t, _P]),
-    "lak_attn_delta_select": (_S, [_P, _I32, _P, _F, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _I32, _P, _P,
-                                   C.c_size_t, _P]),
+    "lak_attn_full": (_S, [_P, _I32, _P, _P, _P, _F, _P, _P, _P, C.c_size_t, _P]),
+    "lak_attn_delta_select": (_S, [_P, _I32, _P, _P, _P, _F, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _I32, _P,
+                                   _P, C.c_size_t, _P]),
     "lak_page_select": (_S, [_P, _P, _I32, _I32, _I32, _P, _P, _I32, _P]),
-    "lak_attn_sparse": (_S, [_P, _I32, _P, _F, _P, _P, _I32, _I32, _P, _P, _P, C.c_size_t, _P]),
+    "lak_attn_sparse": (_S, [_P, _I32, _P, _P, _P, _F, _P, _P, _I32, _I32, _P, _P, _P, C.c_size_t, _P]),
     "lak_trace_decode": (_S, [_P, _P, _P]),
     "lak_last_error": (C.c_char_p, []),
 }

@@ -136,17 +136,20 @@ class PagedKVCache:
             lse = torch.empty((self.batch, self.hq), dtype=torch.float32, device=self.device)
         return out, lse
 
-    def attn_full(self, layer, q, sm_scale, out=None, lse=None):
+    def attn_full(self, layer, q, sm_scale, out=None, lse=None, k_new=None, v_new=None):
+        """Full attention; with k_new / v_new the call also appends this step's token."""
         out, lse = self._out(out, lse)
-        L.check(L.lib().lak_attn_full(self._h, layer, _ptr(q), float(sm_scale), _ptr(out), _ptr(lse),
-                                      _ptr(self.ws), self.ws.numel(), _stream()), "lak_attn_full")
+        L.check(L.lib().lak_attn_full(self._h, layer, _ptr(q), _ptr(k_new), _ptr(v_new), float(sm_scale),
+                                      _ptr(out), _ptr(lse), _ptr(self.ws), self.ws.numel(), _stream()),
+                "lak_attn_full")
         return out, lse
 
     def sel_rows(self, scope):
         return self.hkv if scope == "group" else 1
 
     def attn_delta_select(self, layer, q, sm_scale, k_top, recency, agg="max", scope="group", out=None,
-                          lse=None, sel=None, sel_count=None, page_scores=None, sel_capacity=None):
+                          lse=None, sel=None, sel_count=None, page_scores=None, sel_capacity=None, k_new=None,
+                          v_new=None):
         out, lse = self._out(out, lse)
         R = self.sel_rows(scope)
         cap = sel_capacity or (k_top + recency)
@@ -155,7 +158,8 @@ class PagedKVCache:
         if sel_count is None:
             sel_count = torch.empty((self.batch, R), dtype=torch.int32, device=self.device)
         L.check(L.lib().lak_attn_delta_select(
-            self._h, layer, _ptr(q), float(sm_scale), _ptr(out), _ptr(lse), int(k_top), int(recency), _AGG[agg],
+            self._h, layer, _ptr(q), _ptr(k_new), _ptr(v_new), float(sm_scale), _ptr(out), _ptr(lse), int(k_top),
+            int(recency), _AGG[agg],
             _SCOPE[scope], _ptr(sel), _ptr(sel_count), sel.shape[-1], _ptr(page_scores), _ptr(self.ws),
             self.ws.numel(), _stream()), "lak_attn_delta_select")
         return out, lse, sel, sel_count
@@ -170,9 +174,10 @@ class PagedKVCache:
                                         _ptr(sel), _ptr(sel_count), sel.shape[-1], _stream()), "lak_page_select")
         return sel, sel_count
 
-    def attn_sparse(self, layer, q, sm_scale, sel, sel_count, scope="group", out=None, lse=None):
+    def attn_sparse(self, layer, q, sm_scale, sel, sel_count, scope="group", out=None, lse=None, k_new=None,
+                    v_new=None):
         out, lse = self._out(out, lse)
-        L.check(L.lib().lak_attn_sparse(self._h, layer, _ptr(q), float(sm_scale), _ptr(sel), _ptr(sel_count),
-                                        sel.shape[-1], _SCOPE[scope], _ptr(out), _ptr(lse), _ptr(self.ws),
-                                        self.ws.numel(), _stream()), "lak_attn_sparse")
+        L.check(L.lib().lak_attn_sparse(self._h, layer, _ptr(q), _ptr(k_new), _ptr(v_new), float(sm_scale),
+                                        _ptr(sel), _ptr(sel_count), sel.shape[-1], _SCOPE[scope], _ptr(out),
+                                        _ptr(lse), _ptr(self.ws), self.ws.numel(), _stream()), "lak_attn_sparse")
         return out, lse

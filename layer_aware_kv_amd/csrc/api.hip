@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -34,17 +35,38 @@ lak_status hip_fail(hipError_t e, const char* where) {
   return fail(LAK_EHIP, "%s: %s", where, hipGetErrorString(e));
 }
 
-// Workgroups a split-K launch aims for (about 4 per compute unit on a 256-CU part)
-// and the fewest 16-token sub-tiles one workgroup is given.
+// Workgroups a split-K launch aims for (about 4 per compute unit on a 256-CU part;
+// LAK_TUNE_TARGET_WGS overrides) and the fewest 16-token sub-tiles one workgroup
+// is given.
 constexpr int kTargetWgs = 1024;
 constexpr int kMinSubtilesPerWg = 8;
+// Each of the 4 waves of a decode workgroup keeps the page ids of its items in one
+// register per lane, so a split holds at most 4 * 64 items.
+constexpr int kMaxItemsPerSplit = 256;
 constexpr int kScoreTokensPerBlock = 2048;
 
 int esize(int dtype) { return dtype == LAK_BF16 ? 2 : 4; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+int env_int(const char* name, int dflt, int lo, int hi) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  const int x = std::atoi(v);
+  return (x < lo || x > hi) ? dflt : x;
+}
+
 }  // namespace
+
+int lak::tune_decode_batch() {
+  static const int v = env_int("LAK_TUNE_DECODE_BATCH", 1, 1, 2);
+  return v;
+}
+
+int lak::tune_target_wgs() {
+  static const int v = env_int("LAK_TUNE_TARGET_WGS", kTargetWgs, 64, 65536);
+  return v;
+}
 
 struct lak_cache {
   lak_cache_desc d;
@@ -106,9 +128,10 @@ WsLayout ws_layout(const lak_cache* c) {
 // `max_items` items each.
 int plan_pps(int rows, int max_items, int subtiles_per_page) {
   const int64_t work = (int64_t)rows * max_items;
-  int pps = (int)((work + kTargetWgs - 1) / kTargetWgs);
+  const int target = tune_target_wgs();
+  int pps = (int)((work + target - 1) / target);
   const int min_pps = (kMinSubtilesPerWg + subtiles_per_page - 1) / subtiles_per_page;
-  return std::max(std::max(pps, min_pps), 1);
+  return std::min(std::max(std::max(pps, min_pps), 1), kMaxItemsPerSplit);
 }
 
 lak_status check_cache(const lak_cache* c, bool need_device) {
@@ -144,9 +167,9 @@ lak_status check_ws(const lak_cache* c, const void* ws, size_t ws_bytes) {
 }
 
 // Runs the split-K decode plus combine of one tier.
-lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, float sm_scale,
-                         void* out, float* lse, const int32_t* sel, const int32_t* sel_count,
-                         int sel_cap, int sel_rows, void* ws, hipStream_t st) {
+lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const void* k_new,
+                         const void* v_new, float sm_scale, void* out, float* lse, const int32_t* sel,
+                         const int32_t* sel_count, int sel_cap, int sel_rows, void* ws, hipStream_t st) {
   const auto& d = c->d;
   const WsLayout w = ws_layout(c);
   char* wsb = static_cast<char*>(ws);
@@ -165,6 +188,8 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, float
   a.page_table = d.page_table;
   a.seq_lens = d.seq_lens;
   a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.sm_scale = sm_scale;
   a.hq = d.num_q_heads;
   a.hkv = d.num_kv_heads;
@@ -285,7 +310,9 @@ lak_status lak_cache_create(const lak_cache_desc* desc, lak_cache** out) {
   c->pages.resize(d.max_batch);
   c->lens.assign(d.max_batch, 0);
   c->reset_free_list();
-  c->s_cap = std::min((kTargetWgs + d.num_kv_heads - 1) / d.num_kv_heads, d.max_pages_per_seq);
+  c->s_cap = std::min(std::max((tune_target_wgs() + d.num_kv_heads - 1) / d.num_kv_heads,
+                               (d.max_pages_per_seq + kMaxItemsPerSplit - 1) / kMaxItemsPerSplit),
+                      d.max_pages_per_seq);
   *out = c;
   return ok();
 }
@@ -465,20 +492,21 @@ lak_status lak_kv_gather(lak_cache* c, int32_t layer, int32_t b, int32_t g, int3
   return ok();
 }
 
-lak_status lak_attn_full(lak_cache* c, int32_t layer, const void* q, float sm_scale, void* out, float* lse,
-                         void* ws, size_t ws_bytes, void* stream) {
+lak_status lak_attn_full(lak_cache* c, int32_t layer, const void* q, const void* k_new, const void* v_new,
+                         float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   lak_status s = check_cache(c, true);
   if (s != LAK_OK) return s;
   if ((s = check_layer(c, layer)) != LAK_OK) return s;
   if (c->batch == 0) return ok();
   if (!q || !out) return fail(LAK_EINVAL, "q / out is NULL");
+  if ((k_new == nullptr) != (v_new == nullptr)) return fail(LAK_EINVAL, "give both k_new and v_new or neither");
   if ((s = check_ws(c, ws, ws_bytes)) != LAK_OK) return s;
-  return run_attention(c, layer, MODE_FULL, q, sm_scale, out, lse, nullptr, nullptr, 0, 1, ws,
+  return run_attention(c, layer, MODE_FULL, q, k_new, v_new, sm_scale, out, lse, nullptr, nullptr, 0, 1, ws,
                        static_cast<hipStream_t>(stream));
 }
 
-lak_status lak_attn_delta_select(lak_cache* c, int32_t layer, const void* q, float sm_scale, void* out,
-                                 float* lse, int32_t k_top, int32_t recency, int32_t agg, int32_t scope,
+lak_status lak_attn_delta_select(lak_cache* c, int32_t layer, const void* q, const void* k_new,
+                                 const void* v_new, float sm_scale, void* out, float* lse, int32_t k_top, int32_t recency, int32_t agg, int32_t scope,
                                  int32_t* sel, int32_t* sel_count, int32_t sel_capacity, float* page_scores,
                                  void* ws, size_t ws_bytes, void* stream) {
   lak_status s = check_cache(c, true);
@@ -486,11 +514,12 @@ lak_status lak_attn_delta_select(lak_cache* c, int32_t layer, const void* q, flo
   if ((s = check_layer(c, layer)) != LAK_OK) return s;
   if (!q || !out) return fail(LAK_EINVAL, "q / out is NULL");
   if (agg != LAK_AGG_MAX && agg != LAK_AGG_SUM) return fail(LAK_EINVAL, "bad agg %d", agg);
+  if ((k_new == nullptr) != (v_new == nullptr)) return fail(LAK_EINVAL, "give both k_new and v_new or neither");
   if ((s = check_select_args(c, scope, k_top, recency, sel, sel_count, sel_capacity)) != LAK_OK) return s;
   if (c->batch == 0) return ok();
   if ((s = check_ws(c, ws, ws_bytes)) != LAK_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  s = run_attention(c, layer, MODE_DELTA, q, sm_scale, out, lse, nullptr, nullptr, 0, 1, ws, st);
+  s = run_attention(c, layer, MODE_DELTA, q, k_new, v_new, sm_scale, out, lse, nullptr, nullptr, 0, 1, ws, st);
   if (s != LAK_OK) return s;
   const WsLayout w = ws_layout(c);
   char* wsb = static_cast<char*>(ws);
@@ -524,9 +553,9 @@ lak_status lak_page_select(lak_cache* c, const float* page_scores, int32_t scope
                     static_cast<hipStream_t>(stream));
 }
 
-lak_status lak_attn_sparse(lak_cache* c, int32_t layer, const void* q, float sm_scale, const int32_t* sel,
-                           const int32_t* sel_count, int32_t sel_capacity, int32_t scope, void* out, float* lse,
-                           void* ws, size_t ws_bytes, void* stream) {
+lak_status lak_attn_sparse(lak_cache* c, int32_t layer, const void* q, const void* k_new, const void* v_new,
+                           float sm_scale, const int32_t* sel, const int32_t* sel_count, int32_t sel_capacity,
+                           int32_t scope, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   lak_status s = check_cache(c, true);
   if (s != LAK_OK) return s;
   if ((s = check_layer(c, layer)) != LAK_OK) return s;
@@ -535,10 +564,11 @@ lak_status lak_attn_sparse(lak_cache* c, int32_t layer, const void* q, float sm_
   if (!sel || !sel_count) return fail(LAK_EINVAL, "sel / sel_count is NULL");
   if (sel_capacity <= 0) return fail(LAK_EINVAL, "sel_capacity must be > 0");
   if (scope != LAK_SCOPE_GROUP && scope != LAK_SCOPE_ALL) return fail(LAK_EINVAL, "bad scope %d", scope);
+  if ((k_new == nullptr) != (v_new == nullptr)) return fail(LAK_EINVAL, "give both k_new and v_new or neither");
   if ((s = check_ws(c, ws, ws_bytes)) != LAK_OK) return s;
   const int sel_rows = scope == LAK_SCOPE_GROUP ? c->d.num_kv_heads : 1;
-  return run_attention(c, layer, MODE_SPARSE, q, sm_scale, out, lse, sel, sel_count, sel_capacity, sel_rows, ws,
-                       static_cast<hipStream_t>(stream));
+  return run_attention(c, layer, MODE_SPARSE, q, k_new, v_new, sm_scale, out, lse, sel, sel_count, sel_capacity,
+                       sel_rows, ws, static_cast<hipStream_t>(stream));
 }
 
 lak_status lak_trace_decode(lak_cache* c, void* before, void* after) {

@@ -19,6 +19,15 @@
 
 namespace lak {
 
+// 16-byte fragment load.  STREAM marks it non-temporal: the K/V stream of a full
+// pass (gigabytes) then does not evict from the caches what is reused soon (the
+// delta-layer logits, the page table, the partials).
+template <bool STREAM>
+__device__ inline u32x4 load16(const u32x4* p) {
+  if (STREAM) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
 template <int ESZ, int D>
 struct Frag;
 
@@ -31,13 +40,14 @@ struct Frag<2, D> {
   u32x4 k[NL], v[NL];
   typedef bf16x8 QF;
 
+  template <bool STREAM>
   __device__ inline void load(const uint16_t* kb, const uint16_t* vb, int lane) {
     const u32x4* kp = reinterpret_cast<const u32x4*>(kb);
     const u32x4* vp = reinterpret_cast<const u32x4*>(vb);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) k[i] = kp[i * 64 + lane];
+    for (int i = 0; i < NL; ++i) k[i] = load16<STREAM>(kp + i * 64 + lane);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) v[i] = vp[i * 64 + lane];
+    for (int i = 0; i < NL; ++i) v[i] = load16<STREAM>(vp + i * 64 + lane);
   }
   // lane l: head l%16, head-dim chunk (4i + l/16)*8 .. +8
   __device__ static inline void load_q(QF* qf, const uint16_t* qrow, bool valid, int j) {
@@ -69,6 +79,25 @@ struct Frag<2, D> {
       }
     }
   }
+  // replace token tt of this sub-tile by the row (kr, vr) in the fragments
+  __device__ inline void patch(const uint16_t* kr, const uint16_t* vr, int tt, int lane) {
+    const int n = lane & 15, j = lane >> 4;
+    if (n == tt) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) k[i] = *reinterpret_cast<const u32x4*>(kr + (4 * i + j) * 8);
+    }
+    if (j == tt / 4) {
+      const int e = tt & 3;
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t val = vr[16 * (2 * i + h) + n];
+          const int x = h * 4 + e, sh = 16 * (x & 1);
+          v[i][x >> 1] = (v[i][x >> 1] & ~(0xFFFFu << sh)) | (val << sh);
+        }
+    }
+  }
   __device__ inline void pv(f32x4* o, const float* p) const {
     const uint32_t w0 = (uint32_t)f32_to_bf16_rne(p[0]) | ((uint32_t)f32_to_bf16_rne(p[1]) << 16);
     const uint32_t w1 = (uint32_t)f32_to_bf16_rne(p[2]) | ((uint32_t)f32_to_bf16_rne(p[3]) << 16);
@@ -92,13 +121,14 @@ struct Frag<4, D> {
   u32x4 k[NL], v[NL];
   typedef f32x4 QF;
 
+  template <bool STREAM>
   __device__ inline void load(const uint32_t* kb, const uint32_t* vb, int lane) {
     const u32x4* kp = reinterpret_cast<const u32x4*>(kb);
     const u32x4* vp = reinterpret_cast<const u32x4*>(vb);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) k[i] = kp[i * 64 + lane];
+    for (int i = 0; i < NL; ++i) k[i] = load16<STREAM>(kp + i * 64 + lane);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) v[i] = vp[i * 64 + lane];
+    for (int i = 0; i < NL; ++i) v[i] = load16<STREAM>(vp + i * 64 + lane);
   }
   // lane l: head l%16, head-dim elements 16i + 4(l/16) .. +4
   __device__ static inline void load_q(QF* qf, const uint32_t* qrow, bool valid, int j) {
@@ -126,6 +156,17 @@ struct Frag<4, D> {
         for (int i = 0; i < NL; ++i) v[i][e] = 0u;
       }
   }
+  __device__ inline void patch(const uint32_t* kr, const uint32_t* vr, int tt, int lane) {
+    const int n = lane & 15, j = lane >> 4;
+    if (n == tt) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) k[i] = *reinterpret_cast<const u32x4*>(kr + (4 * i + j) * 4);
+    }
+    if (j == tt / 4) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) v[i][tt & 3] = vr[16 * i + n];
+    }
+  }
   __device__ inline void pv(f32x4* o, const float* p) const {
 #pragma unroll
     for (int i = 0; i < NL; ++i)
@@ -142,8 +183,9 @@ struct ElemT<2> { typedef uint16_t T; };
 template <>
 struct ElemT<4> { typedef uint32_t T; };
 
-template <int ESZ, int D, int MODE>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+// At least 4 waves per SIMD for the single-sub-tile batch (register budget 128).
+template <int ESZ, int D, int MODE, int U>
+__global__ __launch_bounds__(256, (U == 1 ? 4 : 3)) void decode_kernel(DecodeArgs a) {
   typedef typename ElemT<ESZ>::T E;
   typedef Frag<ESZ, D> F;
   extern __shared__ __align__(16) float lds[];
@@ -161,11 +203,34 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     n_items = min(max(a.sel_count[row], 0), min(a.sel_cap, NP));
     sel_row = a.sel + row * a.sel_cap;
   }
+  // Fused append: split 0 of each (b, g) writes this step's token at T-1 into the
+  // pool for later calls; the wave that attends over that sub-tile in this call
+  // takes the token from k_new / v_new directly (see `patch` below).
+  const E* krow_new = nullptr;
+  const E* vrow_new = nullptr;
+  if (a.k_new != nullptr && T > 0) {
+    krow_new = reinterpret_cast<const E*>(a.k_new) + ((int64_t)b * a.hkv + g) * D;
+    vrow_new = reinterpret_cast<const E*>(a.v_new) + ((int64_t)b * a.hkv + g) * D;
+    if (s == 0) {
+      const int t = T - 1;
+      const int64_t phys = a.page_table[(int64_t)b * a.max_pages + t / P];
+      const int64_t base = ((phys * a.hkv + g) * P + ((t % P) / kSub) * kSub) * (int64_t)D;
+      E* kp = const_cast<E*>(reinterpret_cast<const E*>(a.k_pool));
+      E* vp = const_cast<E*>(reinterpret_cast<const E*>(a.v_pool));
+      for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        kp[base + k_off<ESZ>(t % kSub, d)] = krow_new[d];
+        vp[base + v_off<ESZ>(t % kSub, d)] = vrow_new[d];
+      }
+    }
+  }
+
   const int i0 = s * a.pps;
   const int i1 = min(i0 + a.pps, n_items);
   if (i0 >= i1) return;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave index made wave-uniform so that all per-sub-tile bookkeeping is scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
   const bool head_ok = n < G;
 
@@ -177,23 +242,44 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const E* vpool = reinterpret_cast<const E*>(a.v_pool);
   const int32_t* ptab = a.page_table + (int64_t)b * a.max_pages;
   const int spp = P / kSub;
-  const int n_sub = (i1 - i0) * spp;
   const float qk_scale2 = a.sm_scale * kLog2e;
 
-  auto resolve = [&](int u, int64_t& base, int& t0) -> bool {
-    if (u >= n_sub) return false;
-    const int it = u / spp;
-    const int sub = u - it * spp;
-    int lp = i0 + it;
-    if (MODE == MODE_SPARSE) {
-      lp = sel_row[i0 + it];
-      if (lp < 0 || lp >= NP) return false;
+  // This wave takes items i0 + wave + kWaves*k, k < n_w (n_w <= 64: the host caps the
+  // items per split).  Lane k fetches the logical and physical page of its item once;
+  // each sub-tile then reads them with v_readlane (no memory access in the loop).
+  const int n_w = max(0, (i1 - i0 - wave + kWaves - 1) / kWaves);
+  const int nsub = n_w * spp;
+  int lp_vec = -1, pid_vec = 0;
+  if (lane < n_w) {
+    const int it = i0 + wave + kWaves * lane;
+    int lp = (MODE == MODE_SPARSE) ? sel_row[it] : it;
+    if (lp >= 0 && lp < NP) {
+      lp_vec = lp;
+      pid_vec = ptab[lp];
     }
-    t0 = lp * P + sub * kSub;
-    if (t0 >= T) return false;
-    const int64_t phys = ptab[lp];
-    base = ((phys * a.hkv + g) * P + sub * kSub) * (int64_t)D;
-    return true;
+  }
+
+  // The ids (and q) are in registers before the loop: wait for them once here, so
+  // that reading them inside the loop never waits on the K/V loads in flight.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+  struct Sub {
+    bool valid;
+    int t0;
+  };
+  // Issues the K/V loads of sub-tile x (< nsub).  The loads are issued even for a
+  // sub-tile that has no valid token (then from the pool's first sub-tile, always
+  // mapped) so that the steady-state loop issues the same loads on every path.
+  auto issue = [&](F& f, int x) -> Sub {
+    const int k = x / spp;
+    const int sub = x - k * spp;
+    const int lp = __builtin_amdgcn_readlane(lp_vec, k);
+    const int t0 = lp * P + sub * kSub;
+    const bool valid = lp >= 0 && t0 < T;
+    const int64_t phys = __builtin_amdgcn_readlane(pid_vec, k);
+    const int64_t base = valid ? ((phys * a.hkv + g) * P + sub * kSub) * (int64_t)D : 0;
+    f.template load<MODE != MODE_SPARSE>(kpool + base, vpool + base, lane);
+    return Sub{valid, t0};
   };
 
   float m2 = -INFINITY;  // running max, log2 units
@@ -202,55 +288,57 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int x = 0; x < F::NO; ++x) o[x] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  F cur, nxt;
-  int64_t cb = 0, nb = 0;
-  int ct = 0, nt = 0;
-  int u = wave;
-  bool cv = resolve(u, cb, ct);
-  if (cv) cur.load(kpool + cb, vpool + cb, lane);
-  while (u < n_sub) {
-    const int un = u + kWaves;
-    const bool nv = resolve(un, nb, nt);
-    if (nv) nxt.load(kpool + nb, vpool + nb, lane);
-    if (cv) {
-      const f32x4 sacc = cur.qk(qf);
-      const int tb = ct + 4 * j;
-      float s2[4];
-      float mx = -INFINITY;
+  auto process = [&](F& f, int ct) {
+    if (krow_new != nullptr && T - 1 < ct + kSub) f.patch(krow_new, vrow_new, (T - 1) - ct, lane);
+    const f32x4 sacc = f.qk(qf);
+    const int tb = ct + 4 * j;
+    float s2[4];
+    float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s2[r] = (tb + r < T) ? sacc[r] * qk_scale2 : -INFINITY;
-        mx = fmaxf(mx, s2[r]);
-      }
-      if (MODE == MODE_DELTA && head_ok) {
-        f32x4 w;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = (tb + r < T) ? sacc[r] * a.sm_scale : -INFINITY;
-        *reinterpret_cast<f32x4*>(a.logits + ((int64_t)b * a.hq + g * G + n) * a.t_pad + tb) = w;
-      }
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const float m_new = fmaxf(m2, mx);
-      const float alpha = exp2f(m2 - m_new);
-      float p[4];
-      float ps = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = exp2f(s2[r] - m_new);
-        ps += p[r];
-      }
-      l = l * alpha + ps;
-      m2 = m_new;
-#pragma unroll
-      for (int x = 0; x < F::NO; ++x) o[x] *= alpha;
-      if (ct + kSub > T) cur.mask_v(T - ct, j);
-      cur.pv(o, p);
+    for (int r = 0; r < 4; ++r) {
+      s2[r] = (tb + r < T) ? sacc[r] * qk_scale2 : -INFINITY;
+      mx = fmaxf(mx, s2[r]);
     }
-    cur = nxt;
-    cv = nv;
-    cb = nb;
-    ct = nt;
-    u = un;
+    if (MODE == MODE_DELTA && head_ok) {
+      f32x4 w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = (tb + r < T) ? sacc[r] * a.sm_scale : -INFINITY;
+      // plain stores: the logits stay cache-resident for the page-score kernel
+      *reinterpret_cast<f32x4*>(a.logits + ((int64_t)b * a.hq + g * G + n) * a.t_pad + tb) = w;
+    }
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const float m_new = fmaxf(m2, mx);
+    const float alpha = exp2f(m2 - m_new);
+    float p[4];
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = exp2f(s2[r] - m_new);
+      ps += p[r];
+    }
+    l = l * alpha + ps;
+    m2 = m_new;
+#pragma unroll
+    for (int x = 0; x < F::NO; ++x) o[x] *= alpha;
+    if (ct + kSub > T) f.mask_v(T - ct, j);
+    f.pv(o, p);
+  };
+
+  // U sub-tiles per batch: their loads are issued together (unconditionally, so
+  // the wait before each sub-tile is exact) and consumed in order; other waves of
+  // the CU cover the latency between batches.
+  for (int x = 0; x < nsub; x += U) {
+    F buf[U];
+    Sub info[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      info[u] = issue(buf[u], min(x + u, nsub - 1));
+      info[u].valid = info[u].valid && (x + u < nsub);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (info[u].valid) process(buf[u], info[u].t0);
   }
 
   l += shfl_xor_f(l, 16);
@@ -293,10 +381,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// One (head, sequence) per block, one head-dim element per thread.
-template <int ESZ>
-__global__ void combine_kernel(CombineArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x, D = blockDim.x;
+// One wave per (head, sequence).  Lane s holds split s's weight; the weighted sum
+// over splits runs in split order with the weight broadcast from a scalar register
+// and all split loads of an unrolled group in flight together.
+template <int ESZ, int D>
+__global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
+  constexpr int PER = D / 64;  // head-dim elements per lane
+  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int G = a.hq / a.hkv, g = h / G;
   const int T = a.seq_lens[b];
   int n_items;
@@ -309,26 +400,70 @@ __global__ void combine_kernel(CombineArgs a) {
   const int S = min((n_items + a.pps - 1) / a.pps, a.splits);
   const int64_t row0 = ((int64_t)b * a.hq + h) * a.s_cap;
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, a.ml_part[(row0 + s) * 2]);
-  float acc = 0.f, L = 0.f;
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, a.ml_part[(row0 + s) * 2]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float L = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float f = exp2f(a.ml_part[(row0 + s) * 2] - M);
-      L += f * a.ml_part[(row0 + s) * 2 + 1];
-      acc += f * a.o_part[(row0 + s) * D + d];
+    for (int c0 = 0; c0 < S; c0 += 64) {
+      const int s_l = c0 + lane;
+      float wl = 0.f;
+      if (s_l < S) {
+        wl = exp2f(a.ml_part[(row0 + s_l) * 2] - M);
+        L += wl * a.ml_part[(row0 + s_l) * 2 + 1];
+      }
+      const int cn = min(64, S - c0);
+      const float* op = a.o_part + (row0 + c0) * D + lane * PER;
+      int s = 0;
+      for (; s + 8 <= cn; s += 8) {
+        float v[8][PER];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int e = 0; e < PER; ++e) v[u][e] = op[(int64_t)(s + u) * D + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s + u));
+#pragma unroll
+          for (int e = 0; e < PER; ++e) acc[e] += w * v[u][e];
+        }
+      }
+      for (; s < cn; ++s) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s));
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] += w * op[(int64_t)s * D + e];
+      }
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) L += shfl_xor_f(L, o);
   }
-  const float val = (L > 0.f) ? acc / L : 0.f;
-  const int64_t oi = ((int64_t)b * a.hq + h) * D + d;
-  if (ESZ == 2)
-    reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_rne(val);
-  else
-    reinterpret_cast<float*>(a.out)[oi] = val;
-  if (d == 0) {
+  const int64_t oi = ((int64_t)b * a.hq + h) * D + lane * PER;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const float val = (L > 0.f) ? acc[e] / L : 0.f;
+    if (ESZ == 2)
+      reinterpret_cast<uint16_t*>(a.out)[oi + e] = f32_to_bf16_rne(val);
+    else
+      reinterpret_cast<float*>(a.out)[oi + e] = val;
+  }
+  if (lane == 0) {
     const float lse = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
     if (a.lse) a.lse[(int64_t)b * a.hq + h] = lse;
     if (a.lse2) a.lse2[(int64_t)b * a.hq + h] = lse;
   }
+}
+
+template <int ESZ, int D, int U>
+static void launch_decode_u(int mode, const DecodeArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+  if (mode == MODE_FULL)
+    hipLaunchKernelGGL((decode_kernel<ESZ, D, MODE_FULL, U>), grid, dim3(256), lds, st, a);
+  else if (mode == MODE_DELTA)
+    hipLaunchKernelGGL((decode_kernel<ESZ, D, MODE_DELTA, U>), grid, dim3(256), lds, st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<ESZ, D, MODE_SPARSE, U>), grid, dim3(256), lds, st, a);
 }
 
 template <int ESZ, int D>
@@ -337,12 +472,10 @@ static hipError_t launch_decode_t(int mode, const DecodeArgs& a, int splits, int
   const int G = a.hq / a.hkv;
   const size_t lds = (size_t)(kWaves * G * D + 2 * kWaves * 16) * sizeof(float);
   dim3 grid(splits, a.hkv, batch);
-  if (mode == MODE_FULL)
-    hipLaunchKernelGGL((decode_kernel<ESZ, D, MODE_FULL>), grid, dim3(256), lds, st, a);
-  else if (mode == MODE_DELTA)
-    hipLaunchKernelGGL((decode_kernel<ESZ, D, MODE_DELTA>), grid, dim3(256), lds, st, a);
+  if (tune_decode_batch() == 2)
+    launch_decode_u<ESZ, D, 2>(mode, a, grid, lds, st);
   else
-    hipLaunchKernelGGL((decode_kernel<ESZ, D, MODE_SPARSE>), grid, dim3(256), lds, st, a);
+    launch_decode_u<ESZ, D, 1>(mode, a, grid, lds, st);
   return hipGetLastError();
 }
 
@@ -362,10 +495,11 @@ hipError_t launch_decode(int dtype, int mode, int D, const DecodeArgs& a, int sp
 hipError_t launch_combine(int dtype, int D, const CombineArgs& a, int batch, hipStream_t st) {
   if (batch == 0) return hipSuccess;
   dim3 grid(a.hq, batch);
-  if (dtype == 0)
-    hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(D), 0, st, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(D), 0, st, a);
+  if (dtype == 0 && D == 128) hipLaunchKernelGGL((combine_kernel<2, 128>), grid, dim3(64), 0, st, a);
+  else if (dtype == 0 && D == 64) hipLaunchKernelGGL((combine_kernel<2, 64>), grid, dim3(64), 0, st, a);
+  else if (dtype == 1 && D == 128) hipLaunchKernelGGL((combine_kernel<4, 128>), grid, dim3(64), 0, st, a);
+  else if (dtype == 1 && D == 64) hipLaunchKernelGGL((combine_kernel<4, 64>), grid, dim3(64), 0, st, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -15,6 +15,8 @@ struct DecodeArgs {
   const int32_t* page_table;   // [max_batch][max_pages]
   const int32_t* seq_lens;     // [max_batch]
   const void* q;               // [B][Hq][D]
+  const void* k_new;           // optional [B][Hkv][D]: token appended at T-1 by this call
+  const void* v_new;
   float sm_scale;
   int hq, hkv, page, max_pages;
   int pps;                     // items (pages or selection entries) per split
@@ -77,6 +79,12 @@ struct StepUpdate {
 struct KvGeom {
   int hkv, d, page, max_pages, esz;
 };
+
+// Tuning knobs, read once from the environment (defaults are the tuned values):
+//   LAK_TUNE_DECODE_BATCH  sub-tiles loaded together per wave in the decode loop (1 or 2)
+//   LAK_TUNE_TARGET_WGS    workgroups a split-K decode launch aims for
+int tune_decode_batch();
+int tune_target_wgs();
 
 // launchers (return hipSuccess or the launch error)
 hipError_t launch_decode(int dtype, int mode, int D, const DecodeArgs& a, int splits, int batch,

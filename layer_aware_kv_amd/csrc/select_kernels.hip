@@ -9,11 +9,13 @@
 
 namespace lak {
 
-// One block = `tokens_per_block` consecutive tokens of one score row; one token per
-// thread per pass; the page sum is a butterfly over the P lanes of the page
-// (fixed order, so scores are bitwise reproducible).
+// One block = `tokens_per_block` consecutive tokens of one score row; each thread
+// takes 4 consecutive tokens (one 16-byte load per head), so a page of P tokens is
+// P/4 adjacent lanes and its sum is a butterfly over them (fixed order: scores are
+// bitwise reproducible).
 template <int P>
 __global__ __launch_bounds__(256) void page_score_kernel(PageScoreArgs a) {
+  static_assert(P % 4 == 0 && P / 4 <= 64, "page of 4..256 tokens");
   const int chunk = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const int T = a.seq_lens[b];
   const int NP = min((T + P - 1) / P, a.max_pages);
@@ -27,18 +29,39 @@ __global__ __launch_bounds__(256) void page_score_kernel(PageScoreArgs a) {
   float* out = a.scores + ((int64_t)b * rows + r) * a.max_pages;
   const int tb0 = chunk * a.tokens_per_block;
   const int tb1 = min(tb0 + a.tokens_per_block, t_end);
-  for (int base = tb0; base < tb1; base += blockDim.x) {
-    const int t = base + threadIdx.x;
-    float acc = 0.f;
-    if (t < T && t < tb1) {
-      for (int hh = 0; hh < nh; ++hh) {
-        const float w = expf(lg[(int64_t)hh * a.t_pad + t] - ls[hh]);
-        acc = (a.agg == 0) ? fmaxf(acc, w) : acc + w;
+  for (int base = tb0; base < tb1; base += 4 * blockDim.x) {
+    const int t = base + 4 * threadIdx.x;  // first of this thread's 4 tokens
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (t < tb1) {
+      int hh = 0;
+      for (; hh + 4 <= nh; hh += 4) {
+        f32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4*>(lg + (int64_t)(hh + u) * a.t_pad + t);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float lse = ls[hh + u];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float w = (t + e < T) ? expf(v[u][e] - lse) : 0.f;
+            acc[e] = (a.agg == 0) ? fmaxf(acc[e], w) : acc[e] + w;
+          }
+        }
+      }
+      for (; hh < nh; ++hh) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(lg + (int64_t)hh * a.t_pad + t);
+        const float lse = ls[hh];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float w = (t + e < T) ? expf(v[e] - lse) : 0.f;
+          acc[e] = (a.agg == 0) ? fmaxf(acc[e], w) : acc[e] + w;
+        }
       }
     }
+    float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
 #pragma unroll
-    for (int o = 1; o < P; o <<= 1) acc += shfl_xor_f(acc, o);
-    if ((t % P) == 0 && t < tb1) out[t / P] = acc;
+    for (int o = 1; o < P / 4; o <<= 1) sum += shfl_xor_f(sum, o);
+    if ((t % P) == 0 && t < tb1) out[t / P] = sum;
   }
 }
 
@@ -60,6 +83,7 @@ hipError_t launch_page_score(const PageScoreArgs& a, int batch, int rows, int ma
 // zero, negative and NaN scores all map to 0.
 __device__ inline uint32_t score_key(float x) { return (x > 0.f) ? __float_as_uint(x) : 0u; }
 
+// Exclusive prefix sum over the block (blockDim.x a multiple of 64, at most 1024).
 __device__ inline int block_excl_scan(int v, int* total, int* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
@@ -76,15 +100,22 @@ __device__ inline int block_excl_scan(int v, int* total, int* wsum) {
   return base + inc - v;
 }
 
-// One score row per block (256 threads).  Radix select (4 passes of 8 bits, most
-// significant first) finds tau, the key of the kk-th largest candidate, and how
-// many candidates equal to tau are still needed; those are taken in ascending page
-// order (lower index wins ties).  A block-wide scan then writes the selected pages
-// (older winners and the recency window) in ascending order.
-__global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkLdsKeys = 12288;  // rows up to this many pages are staged in LDS (48 KiB)
+
+// One score row per block.  The row's order keys are staged in LDS once (rows
+// longer than kTopkLdsKeys are read from global memory instead).  Radix select (4
+// passes of 8 bits, most significant first) finds tau, the key of the kk-th
+// largest candidate, and how many candidates equal to tau are still needed; those
+// are taken in ascending page order (lower index wins ties).  A block-wide scan
+// then writes the selected pages (older winners and the recency window) in
+// ascending order.
+template <bool IN_LDS>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
+  extern __shared__ uint32_t lds_keys[];
   __shared__ int hist[256];
   __shared__ int sh_bin, sh_rem;
-  __shared__ int wsum[8];
+  __shared__ int wsum[kTopkThreads / 64];
   const int r = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.seq_lens[b];
@@ -97,17 +128,23 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const bool all_c = (kk == NC);
   const bool radix = !all_c && kk > 0;
 
+  if (IN_LDS) {
+    for (int jj = tid; jj < NC; jj += blockDim.x) lds_keys[jj] = score_key(S[jj]);
+    __syncthreads();
+  }
+  auto key = [&](int jj) -> uint32_t { return IN_LDS ? lds_keys[jj] : score_key(S[jj]); };
+
   uint32_t tau = 0;
   int need_eq = 0;
   if (radix) {
     uint32_t prefix = 0, mask = 0;
     int rem = kk;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
+      if (tid < 256) hist[tid] = 0;
       __syncthreads();
       for (int jj = tid; jj < NC; jj += blockDim.x) {
-        const uint32_t key = score_key(S[jj]);
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+        const uint32_t k = key(jj);
+        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
       }
       __syncthreads();
       if (wave == 0) {
@@ -145,16 +182,16 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const int j0 = min(tid * E, NP), j1 = min(j0 + E, NP);
   int eqc = 0;
   if (radix)
-    for (int jj = j0; jj < min(j1, NC); ++jj) eqc += (score_key(S[jj]) == tau);
+    for (int jj = j0; jj < min(j1, NC); ++jj) eqc += (key(jj) == tau);
   int dummy;
   const int eq_base = block_excl_scan(eqc, &dummy, wsum);
 
   auto flag = [&](int jj, int& eqr) -> bool {
     if (jj >= NC || all_c) return true;
     if (!radix) return false;
-    const uint32_t key = score_key(S[jj]);
-    if (key > tau) return true;
-    if (key == tau) return (eqr++) < need_eq;
+    const uint32_t k = key(jj);
+    if (k > tau) return true;
+    if (k == tau) return (eqr++) < need_eq;
     return false;
   };
   int cnt = 0, eqr = eq_base;
@@ -170,7 +207,11 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 
 hipError_t launch_topk(const TopkArgs& a, int batch, hipStream_t st) {
   if (batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3(a.rows_per_seq, batch), dim3(256), 0, st, a);
+  dim3 grid(a.rows_per_seq, batch);
+  if (a.max_pages <= kTopkLdsKeys)
+    hipLaunchKernelGGL(topk_kernel<true>, grid, dim3(kTopkThreads), (size_t)a.max_pages * 4, st, a);
+  else
+    hipLaunchKernelGGL(topk_kernel<false>, grid, dim3(kTopkThreads), 0, st, a);
   return hipGetLastError();
 }
 

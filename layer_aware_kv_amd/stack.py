@@ -33,7 +33,8 @@ class DeltaStack:
     selection installed by delta-layer l in ``sel[l]`` / ``sel_count[l]``.
     """
 
-    def __init__(self, cache: PagedKVCache, tiers, k_top, recency, sm_scale, agg="max", scope="group"):
+    def __init__(self, cache: PagedKVCache, tiers, k_top, recency, sm_scale, agg="max", scope="group",
+                 fused_append=True):
         if tiers and tiers[0] == "sparse":
             raise ValueError("a stack cannot start with a sparse layer")
         first_delta = next((i for i, t in enumerate(tiers) if t == "delta"), None)
@@ -44,6 +45,7 @@ class DeltaStack:
         self.tiers = list(tiers)
         self.k_top, self.recency, self.sm_scale = k_top, recency, sm_scale
         self.agg, self.scope = agg, scope
+        self.fused_append = fused_append  # append inside the attention call (one launch fewer)
         B, L = cache.max_batch, len(tiers)
         dev = cache.device
         self.out = torch.zeros((L, B, cache.hq, cache.d), dtype=cache.torch_dtype, device=dev)
@@ -65,19 +67,23 @@ class DeltaStack:
         c.step_begin()
         cur = None
         for layer, tier in enumerate(self.tiers):
-            c.kv_append(layer, k_new[layer], v_new[layer])
+            if self.fused_append:
+                kn, vn = k_new[layer], v_new[layer]
+            else:
+                c.kv_append(layer, k_new[layer], v_new[layer])
+                kn = vn = None
             out, lse = self.out[layer, :B], self.lse[layer, :B]
             ev = tracer.pair(layer, tier) if tracer is not None else None
             if ev is not None:
                 c.trace_decode(*ev)
             if tier == "full":
-                c.attn_full(layer, q[layer], self.sm_scale, out, lse)
+                c.attn_full(layer, q[layer], self.sm_scale, out, lse, kn, vn)
             elif tier == "delta":
                 sel, cnt = self.sel[layer][:B], self.sel_count[layer][:B]
                 c.attn_delta_select(layer, q[layer], self.sm_scale, self.k_top, self.recency, self.agg, self.scope,
-                                    out, lse, sel, cnt)
+                                    out, lse, sel, cnt, k_new=kn, v_new=vn)
                 cur = (sel, cnt)
             else:
-                c.attn_sparse(layer, q[layer], self.sm_scale, cur[0], cur[1], self.scope, out, lse)
+                c.attn_sparse(layer, q[layer], self.sm_scale, cur[0], cur[1], self.scope, out, lse, kn, vn)
             if ev is not None:
                 c.trace_decode()

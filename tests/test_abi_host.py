@@ -123,12 +123,12 @@ def test_allocator_out_of_pages_and_limits():
 def test_attention_calls_on_metadata_only_cache_fail_cleanly():
     lib = L.lib()
     st, h = _create()
-    assert lib.lak_attn_full(h, 0, None, 1.0, None, None, None, 0, None) == L.LAK_ESTATE
+    assert lib.lak_attn_full(h, 0, None, None, None, 1.0, None, None, None, 0, None) == L.LAK_ESTATE
     L.check(lib.lak_seq_reset(h, 1, (C.c_int32 * 1)(5), 0, None), "reset")
     dummy = C.c_void_p(256)
-    assert lib.lak_attn_full(h, 0, dummy, 1.0, dummy, None, dummy, 1 << 20, None) == L.LAK_ESTATE
+    assert lib.lak_attn_full(h, 0, dummy, None, None, 1.0, dummy, None, dummy, 1 << 20, None) == L.LAK_ESTATE
     assert lib.lak_kv_append(h, 0, dummy, dummy, None) == L.LAK_ESTATE
-    assert lib.lak_attn_full(None, 0, dummy, 1.0, dummy, None, dummy, 1 << 20, None) == L.LAK_EINVAL
+    assert lib.lak_attn_full(None, 0, dummy, None, None, 1.0, dummy, None, dummy, 1 << 20, None) == L.LAK_EINVAL
     assert lib.lak_workspace_bytes(h) > 0
     lib.lak_cache_destroy(h)
 

@@ -131,7 +131,7 @@ def _tie_scores(rng, B, R, NP, levels):
 
 @pytest.mark.parametrize("NP,k_top,rec,levels", [
     (64, 8, 4, 5), (512, 96, 32, 3), (4100, 192, 64, 50), (1000, 0, 8, 4), (30, 40, 4, 3),
-    (7, 3, 9, 2), (2049, 2048, 0, 2), (300, 17, 0, 1000000)])
+    (7, 3, 9, 2), (2049, 2048, 0, 2), (300, 17, 0, 1000000), (13000, 500, 16, 7)])
 def test_page_select_on_oracle_scores_is_exact(NP, k_top, rec, levels):
     from layer_aware_kv_amd import PagedKVCache
     B, R, P = 3, 2, 16
@@ -264,3 +264,44 @@ def test_deterministic_bitwise():
         res.append([t.clone() for t in (out, lse, sel, cnt, scores, out_s, lse_s)])
     for a, b in zip(*res):
         assert torch.equal(a, b)
+
+
+FUSE_CASES = [CASES[0], CASES[2], CASES[3], CASES[6]]
+
+
+@pytest.mark.parametrize("spec", FUSE_CASES, ids=[c[0] for c in FUSE_CASES])
+def test_fused_append_matches_separate_append(spec):
+    """An attention call given k_new / v_new equals kv_append followed by the call."""
+    case, P, sm = _case(spec)
+    B = len(case.lengths)
+    cache_a = make_cache(case, P)
+    q = fill_and_step(cache_a, case)
+    k_top, rec = _budget(max(case.lengths), P)
+    out_f, lse_f = cache_a.attn_full(0, q, sm)
+    out_d, lse_d, sel, cnt = cache_a.attn_delta_select(0, q, sm, k_top, rec)
+    out_s, lse_s = cache_a.attn_sparse(0, q, sm, sel, cnt)
+    k, v = to_dev(case.K, case.dtype), to_dev(case.V, case.dtype)
+    kn = torch.stack([k[b, :, case.lengths[b] - 1] for b in range(B)]).contiguous()
+    vn = torch.stack([v[b, :, case.lengths[b] - 1] for b in range(B)]).contiguous()
+    for tier in ("full", "delta", "sparse"):
+        cache_b = make_cache(case, P)
+        cache_b.seq_reset([n - 1 for n in case.lengths])
+        cache_b.kv_prefill(0, k, v)
+        cache_b.step_begin()
+        if tier == "full":
+            o, l = cache_b.attn_full(0, q, sm, k_new=kn, v_new=vn)
+            ref = (out_f, lse_f)
+        elif tier == "delta":
+            o, l, s2, c2 = cache_b.attn_delta_select(0, q, sm, k_top, rec, k_new=kn, v_new=vn)
+            ref = (out_d, lse_d)
+        else:
+            o, l = cache_b.attn_sparse(0, q, sm, sel, cnt, k_new=kn, v_new=vn)
+            ref = (out_s, lse_s)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref[0]) and torch.equal(l, ref[1]), tier
+        if tier == "delta":
+            assert torch.equal(s2, sel) and torch.equal(c2, cnt)
+        for b in range(B):
+            for g in range(case.K.shape[1]):
+                kg, vg = cache_b.kv_gather(0, b, g, case.lengths[b] - 1, 1)
+                assert torch.equal(kg[0], kn[b, g]) and torch.equal(vg[0], vn[b, g])
