@@ -58,14 +58,16 @@ int env_int(const char* name, int dflt, int lo, int hi) {
 
 }  // namespace
 
-int lak::tune_decode_batch() {
-  static const int v = env_int("LAK_TUNE_DECODE_BATCH", 1, 1, 2);
-  return v;
+int lak::tune_decode_batch(int mode) {
+  static const int full = env_int("LAK_TUNE_DECODE_BATCH", 1, 1, 2);
+  static const int sparse = env_int("LAK_TUNE_SPARSE_BATCH", 1, 1, 4);
+  return mode == MODE_SPARSE ? (sparse == 3 ? 2 : sparse) : full;
 }
 
-int lak::tune_target_wgs() {
-  static const int v = env_int("LAK_TUNE_TARGET_WGS", kTargetWgs, 64, 65536);
-  return v;
+int lak::tune_target_wgs(int mode) {
+  static const int full = env_int("LAK_TUNE_TARGET_WGS", kTargetWgs, 64, 65536);
+  static const int sparse = env_int("LAK_TUNE_SPARSE_WGS", kTargetWgs, 64, 65536);
+  return mode == MODE_SPARSE ? sparse : full;
 }
 
 struct lak_cache {
@@ -116,8 +118,11 @@ WsLayout ws_layout(const lak_cache* c) {
   off = align256(off + rows_h * c->s_cap * 2 * sizeof(float));
   w.lse = off;
   off = align256(off + rows_h * sizeof(float));
-  w.logits = off;
-  off = align256(off + rows_h * (size_t)d.max_pages_per_seq * d.page_size * sizeof(float));
+  w.logits = off;  // [B][Hkv][sub-tiles][Gp][16], Gp = G rounded up to even
+  const int G = d.num_q_heads / d.num_kv_heads;
+  const size_t gp = (size_t)(G + (G & 1));
+  off = align256(off + (size_t)d.max_batch * d.num_kv_heads * gp * (size_t)d.max_pages_per_seq * d.page_size *
+                           sizeof(float));
   w.scores = off;
   off = align256(off + (size_t)d.max_batch * d.num_kv_heads * d.max_pages_per_seq * sizeof(float));
   w.total = off;
@@ -126,9 +131,9 @@ WsLayout ws_layout(const lak_cache* c) {
 
 // Items (pages or selection entries) per split for `rows` rows of up to
 // `max_items` items each.
-int plan_pps(int rows, int max_items, int subtiles_per_page) {
+int plan_pps(int rows, int max_items, int subtiles_per_page, int mode) {
   const int64_t work = (int64_t)rows * max_items;
-  const int target = tune_target_wgs();
+  const int target = tune_target_wgs(mode);
   int pps = (int)((work + target - 1) / target);
   const int min_pps = (kMinSubtilesPerWg + subtiles_per_page - 1) / subtiles_per_page;
   return std::min(std::max(std::max(pps, min_pps), 1), kMaxItemsPerSplit);
@@ -177,7 +182,7 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
   int max_items = c->max_np();
   if (mode == MODE_SPARSE) max_items = std::min(max_items, sel_cap);
   const int rows = c->batch * d.num_kv_heads;
-  const int pps = plan_pps(rows, max_items, spp);
+  const int pps = plan_pps(rows, max_items, spp, mode);
   const int splits = (max_items + pps - 1) / pps;
   if (splits > c->s_cap) return fail(LAK_EINVAL, "internal: %d splits exceed capacity %d", splits, c->s_cap);
 
@@ -310,7 +315,8 @@ lak_status lak_cache_create(const lak_cache_desc* desc, lak_cache** out) {
   c->pages.resize(d.max_batch);
   c->lens.assign(d.max_batch, 0);
   c->reset_free_list();
-  c->s_cap = std::min(std::max((tune_target_wgs() + d.num_kv_heads - 1) / d.num_kv_heads,
+  c->s_cap = std::min(std::max((std::max(tune_target_wgs(MODE_FULL), tune_target_wgs(MODE_SPARSE)) +
+                                d.num_kv_heads - 1) / d.num_kv_heads,
                                (d.max_pages_per_seq + kMaxItemsPerSplit - 1) / kMaxItemsPerSplit),
                       d.max_pages_per_seq);
   *out = c;

@@ -5,8 +5,8 @@
 //               token (the delta-layer scores are taken from the decode kernel's
 //               own logits, as the pages' implementation does),
 //   MODE_SPARSE attention over the tokens of the selected pages only.
-// One workgroup = one (sequence b, KV head g, split s); its 4 waves take the 16-token
-// sub-tiles of the split in turn.  Per sub-tile: S^T = K Q^T with the G query heads
+// One workgroup = one (sequence b, KV head g, split s); a row's pages are dealt to
+// its splits round-robin and a split's 4 waves take its pages in turn.  Per sub-tile: S^T = K Q^T with the G query heads
 // of the group as the 16-wide MFMA N dimension, online softmax in the log2
 // domain, then O^T += V^T P^T.  K and V fragments come straight from HBM into
 // registers (the pool's in-page order matches the MFMA operand layout, so every
@@ -185,13 +185,14 @@ struct ElemT<4> { typedef uint32_t T; };
 
 // At least 4 waves per SIMD for the single-sub-tile batch (register budget 128).
 template <int ESZ, int D, int MODE, int U>
-__global__ __launch_bounds__(256, (U == 1 ? 4 : 3)) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_kernel(DecodeArgs a) {
   typedef typename ElemT<ESZ>::T E;
   typedef Frag<ESZ, D> F;
   extern __shared__ __align__(16) float lds[];
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = a.hq / a.hkv;
+  const int Gp = G + (G & 1);
   const int T = a.seq_lens[b];
   const int P = a.page;
   const int NP = (T + P - 1) / P;
@@ -224,9 +225,12 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : 3)) void decode_kernel(DecodeArg
     }
   }
 
-  const int i0 = s * a.pps;
-  const int i1 = min(i0 + a.pps, n_items);
-  if (i0 >= i1) return;
+  // The row's items are dealt round-robin to its S_row splits (split s takes items
+  // s, s + S_row, s + 2 S_row, ...): the workgroups of a row then stream neighbouring
+  // pages at the same time, which keeps concurrent DRAM accesses close together.
+  const int S_row = (n_items + a.pps - 1) / a.pps;
+  if (s >= S_row) return;
+  const int n_split = (n_items - s + S_row - 1) / S_row;  // items of this split
 
   // wave index made wave-uniform so that all per-sub-tile bookkeeping is scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -244,14 +248,14 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : 3)) void decode_kernel(DecodeArg
   const int spp = P / kSub;
   const float qk_scale2 = a.sm_scale * kLog2e;
 
-  // This wave takes items i0 + wave + kWaves*k, k < n_w (n_w <= 64: the host caps the
-  // items per split).  Lane k fetches the logical and physical page of its item once;
-  // each sub-tile then reads them with v_readlane (no memory access in the loop).
-  const int n_w = max(0, (i1 - i0 - wave + kWaves - 1) / kWaves);
+  // This wave takes members wave + kWaves*k (k < n_w <= 64: the host caps the items
+  // per split) of its split.  Lane k fetches the logical and physical page of its item
+  // once; each sub-tile then reads them with v_readlane (no memory access in the loop).
+  const int n_w = max(0, (n_split - wave + kWaves - 1) / kWaves);
   const int nsub = n_w * spp;
   int lp_vec = -1, pid_vec = 0;
   if (lane < n_w) {
-    const int it = i0 + wave + kWaves * lane;
+    const int it = s + S_row * (wave + kWaves * lane);
     int lp = (MODE == MODE_SPARSE) ? sel_row[it] : it;
     if (lp >= 0 && lp < NP) {
       lp_vec = lp;
@@ -299,12 +303,16 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : 3)) void decode_kernel(DecodeArg
       s2[r] = (tb + r < T) ? sacc[r] * qk_scale2 : -INFINITY;
       mx = fmaxf(mx, s2[r]);
     }
-    if (MODE == MODE_DELTA && head_ok) {
+    if (MODE == MODE_DELTA && n < Gp) {
+      // Logits block of (b, g, sub-tile): [Gp heads][16 tokens], Gp = G rounded up to
+      // even, so one store instruction writes whole 128-byte lines (the padding head,
+      // if any, is written too).  Plain stores: the block stays cache-resident for the
+      // page-score kernel.
       f32x4 w;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) w[r] = (tb + r < T) ? sacc[r] * a.sm_scale : -INFINITY;
-      // plain stores: the logits stay cache-resident for the page-score kernel
-      *reinterpret_cast<f32x4*>(a.logits + ((int64_t)b * a.hq + g * G + n) * a.t_pad + tb) = w;
+      for (int r = 0; r < 4; ++r) w[r] = (head_ok && tb + r < T) ? sacc[r] * a.sm_scale : -INFINITY;
+      const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + ct / kSub;
+      *reinterpret_cast<f32x4*>(a.logits + (blk * Gp + n) * kSub + 4 * j) = w;
     }
     mx = fmaxf(mx, shfl_xor_f(mx, 16));
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
@@ -472,7 +480,10 @@ static hipError_t launch_decode_t(int mode, const DecodeArgs& a, int splits, int
   const int G = a.hq / a.hkv;
   const size_t lds = (size_t)(kWaves * G * D + 2 * kWaves * 16) * sizeof(float);
   dim3 grid(splits, a.hkv, batch);
-  if (tune_decode_batch() == 2)
+  const int u = tune_decode_batch(mode);
+  if (u == 4)
+    launch_decode_u<ESZ, D, 4>(mode, a, grid, lds, st);
+  else if (u == 2)
     launch_decode_u<ESZ, D, 2>(mode, a, grid, lds, st);
   else
     launch_decode_u<ESZ, D, 1>(mode, a, grid, lds, st);

@@ -29,8 +29,8 @@ struct DecodeArgs {
   // outputs
   float* o_part;               // [B][Hq][s_cap][D]
   float* ml_part;              // [B][Hq][s_cap][2]  (max in log2 units, sum)
-  float* logits;               // delta tier: [B][Hq][t_pad]
-  int64_t t_pad;
+  float* logits;               // delta tier: [B][Hkv][t_pad/16][Gp][16] (Gp = G rounded up to even)
+  int64_t t_pad;               // token capacity of a sequence (max_pages * page)
 };
 
 struct CombineArgs {
@@ -47,7 +47,7 @@ struct CombineArgs {
 };
 
 struct PageScoreArgs {
-  const float* logits;        // [B][Hq][t_pad]
+  const float* logits;        // [B][Hkv][t_pad/16][Gp][16], as written by the decode kernel
   const float* lse;           // [B][Hq]
   const int32_t* seq_lens;
   float* scores;              // [B][R][max_pages]
@@ -81,10 +81,12 @@ struct KvGeom {
 };
 
 // Tuning knobs, read once from the environment (defaults are the tuned values):
-//   LAK_TUNE_DECODE_BATCH  sub-tiles loaded together per wave in the decode loop (1 or 2)
-//   LAK_TUNE_TARGET_WGS    workgroups a split-K decode launch aims for
-int tune_decode_batch();
-int tune_target_wgs();
+//   LAK_TUNE_DECODE_BATCH  sub-tiles loaded together per wave, full / delta tiers (1 or 2)
+//   LAK_TUNE_SPARSE_BATCH  the same for the sparse tier (1, 2 or 4)
+//   LAK_TUNE_TARGET_WGS    workgroups a full / delta split-K launch aims for
+//   LAK_TUNE_SPARSE_WGS    workgroups a sparse split-K launch aims for
+int tune_decode_batch(int mode);
+int tune_target_wgs(int mode);
 
 // launchers (return hipSuccess or the launch error)
 hipError_t launch_decode(int dtype, int mode, int D, const DecodeArgs& a, int splits, int batch,

@@ -10,22 +10,24 @@
 namespace lak {
 
 // One block = `tokens_per_block` consecutive tokens of one score row; each thread
-// takes 4 consecutive tokens (one 16-byte load per head), so a page of P tokens is
-// P/4 adjacent lanes and its sum is a butterfly over them (fixed order: scores are
-// bitwise reproducible).
+// takes 4 consecutive tokens, so a page of P tokens is P/4 adjacent lanes and its
+// sum is a butterfly over them (fixed order: scores are bitwise reproducible).
+// Logits come in the decode kernel's blocks: per (b, KV head g, 16-token sub-tile)
+// [Gp heads][16 tokens], Gp = G rounded up to even.
 template <int P>
 __global__ __launch_bounds__(256) void page_score_kernel(PageScoreArgs a) {
-  static_assert(P % 4 == 0 && P / 4 <= 64, "page of 4..256 tokens");
+  static_assert(P % 16 == 0 && P / 4 <= 64, "page of 16..256 tokens");
   const int chunk = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const int T = a.seq_lens[b];
   const int NP = min((T + P - 1) / P, a.max_pages);
   const int t_end = NP * P;
   const int G = a.hq / a.hkv;
-  const int h0 = a.scope == 0 ? r * G : 0;
-  const int nh = a.scope == 0 ? G : a.hq;
+  const int Gp = G + (G & 1);
+  const int g_lo = a.scope == 0 ? r : 0;
+  const int g_hi = a.scope == 0 ? r + 1 : a.hkv;
   const int rows = a.scope == 0 ? a.hkv : 1;
-  const float* lg = a.logits + ((int64_t)b * a.hq + h0) * a.t_pad;
-  const float* ls = a.lse + (int64_t)b * a.hq + h0;
+  const int64_t nsub = a.t_pad / 16;
+  const float* ls = a.lse + (int64_t)b * a.hq;
   float* out = a.scores + ((int64_t)b * rows + r) * a.max_pages;
   const int tb0 = chunk * a.tokens_per_block;
   const int tb1 = min(tb0 + a.tokens_per_block, t_end);
@@ -33,28 +35,31 @@ __global__ __launch_bounds__(256) void page_score_kernel(PageScoreArgs a) {
     const int t = base + 4 * threadIdx.x;  // first of this thread's 4 tokens
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     if (t < tb1) {
-      int hh = 0;
-      for (; hh + 4 <= nh; hh += 4) {
-        f32x4 v[4];
+      for (int g = g_lo; g < g_hi; ++g) {
+        const float* bp = a.logits + (((int64_t)b * a.hkv + g) * nsub + t / 16) * Gp * 16 + (t % 16);
+        int h = 0;
+        for (; h + 4 <= G; h += 4) {
+          f32x4 v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4*>(lg + (int64_t)(hh + u) * a.t_pad + t);
+          for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4*>(bp + (h + u) * 16);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float lse = ls[hh + u];
+          for (int u = 0; u < 4; ++u) {
+            const float lse = ls[g * G + h + u];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float w = (t + e < T) ? expf(v[u][e] - lse) : 0.f;
-            acc[e] = (a.agg == 0) ? fmaxf(acc[e], w) : acc[e] + w;
+            for (int e = 0; e < 4; ++e) {
+              const float w = (t + e < T) ? expf(v[u][e] - lse) : 0.f;
+              acc[e] = (a.agg == 0) ? fmaxf(acc[e], w) : acc[e] + w;
+            }
           }
         }
-      }
-      for (; hh < nh; ++hh) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(lg + (int64_t)hh * a.t_pad + t);
-        const float lse = ls[hh];
+        for (; h < G; ++h) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(bp + h * 16);
+          const float lse = ls[g * G + h];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float w = (t + e < T) ? expf(v[e] - lse) : 0.f;
-          acc[e] = (a.agg == 0) ? fmaxf(acc[e], w) : acc[e] + w;
+          for (int e = 0; e < 4; ++e) {
+            const float w = (t + e < T) ? expf(v[e] - lse) : 0.f;
+            acc[e] = (a.agg == 0) ? fmaxf(acc[e], w) : acc[e] + w;
+          }
         }
       }
     }
