@@ -142,9 +142,9 @@ class StackBench:
         stack)`` (tests only) runs after every step and is not meant for timing."""
         from layer_aware_kv_amd import DeltaStack
         torch, wl, cache = self.torch, self.wl, self.cache
-        if self.dirty:
-            self.prefill_all()
         cache.seq_reset(self.lens0, reserve_tokens=self.S)
+        if self.dirty:  # a drift event rewrote keys: restore the prefilled state
+            self.prefill_all()
         stack = DeltaStack(cache, tiers, wl.k_top, wl.recency, wl.sm_scale)
 
         def one(s, tr):

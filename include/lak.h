@@ -198,6 +198,37 @@ lak_status lak_attn_sparse(lak_cache* cache, int32_t layer, const void* q, const
                            const int32_t* sel_count, int32_t sel_capacity, int32_t scope, void* out,
                            float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* One decode step of a whole attention stack (the three-tier schedule: "Methodology
+ * in Plain English" -- full layers, delta-layers that refresh the page selection,
+ * sparse layers over the latest selection, recomputed for every generated token).
+ * Performs lak_step_begin, then for every layer l in order: the attention call of
+ * its tier (full / delta-select / sparse with the selection of the latest
+ * delta-layer before l), appending k_new[l] / v_new[l] inside the call.  All host
+ * arrays have num_layers entries of device pointers; lse[l] may be NULL; sel[l] /
+ * sel_count[l] are used (and required) for delta layers only, shaped as in
+ * lak_attn_delta_select with sel_capacity >= k_top + recency.  Everything is
+ * validated before anything is enqueued; errors: EINVAL (bad tier, a sparse layer
+ * before any delta-layer, NULL pointer), plus those of lak_step_begin. */
+typedef struct {
+  int32_t num_layers;
+  const int32_t* tiers;        /* host [num_layers]: 0 full, 1 delta, 2 sparse */
+  const void* const* q;        /* host [num_layers] of device [B][Hq][D] */
+  const void* const* k_new;    /* host [num_layers] of device [B][Hkv][D] */
+  const void* const* v_new;    /* host [num_layers] of device [B][Hkv][D] */
+  void* const* out;            /* host [num_layers] of device [B][Hq][D] */
+  float* const* lse;           /* host [num_layers] of device [B][Hq] (entries may be NULL) */
+  int32_t* const* sel;         /* host [num_layers]: delta layers' device selection buffers */
+  int32_t* const* sel_count;   /* host [num_layers]: delta layers' device counts */
+  int32_t sel_capacity;
+  float sm_scale;
+  int32_t k_top, recency, agg, scope;
+  void* const* trace_before;   /* NULL, or host [num_layers] of hipEvent_t (entries may be NULL): */
+  void* const* trace_after;    /* recorded around layer l's decode kernel as lak_trace_decode does */
+} lak_stack_step_desc;
+
+lak_status lak_stack_step(lak_cache* cache, const lak_stack_step_desc* step, void* ws, size_t ws_bytes,
+                          void* stream);
+
 /* Tracing: while set, every attention call on `cache` records `before` and `after`
  * (hipEvent_t created by the caller) on its stream immediately before and after
  * its split-K decode kernel, so hipEventElapsedTime gives that kernel's duration.

@@ -32,6 +32,18 @@ class CacheDesc(C.Structure):
     ]
 
 
+class StackStepDesc(C.Structure):
+    _fields_ = [
+        ("num_layers", C.c_int32), ("tiers", C.POINTER(C.c_int32)),
+        ("q", C.POINTER(C.c_void_p)), ("k_new", C.POINTER(C.c_void_p)), ("v_new", C.POINTER(C.c_void_p)),
+        ("out", C.POINTER(C.c_void_p)), ("lse", C.POINTER(C.c_void_p)),
+        ("sel", C.POINTER(C.c_void_p)), ("sel_count", C.POINTER(C.c_void_p)),
+        ("sel_capacity", C.c_int32), ("sm_scale", C.c_float),
+        ("k_top", C.c_int32), ("recency", C.c_int32), ("agg", C.c_int32), ("scope", C.c_int32),
+        ("trace_before", C.POINTER(C.c_void_p)), ("trace_after", C.POINTER(C.c_void_p)),
+    ]
+
+
 _P = C.c_void_p
 _I32 = C.c_int32
 _I64 = C.c_int64
@@ -58,6 +70,7 @@ SIGNATURES = {
                                    _P, C.c_size_t, _P]),
     "lak_page_select": (_S, [_P, _P, _I32, _I32, _I32, _P, _P, _I32, _P]),
     "lak_attn_sparse": (_S, [_P, _I32, _P, _P, _P, _F, _P, _P, _I32, _I32, _P, _P, _P, C.c_size_t, _P]),
+    "lak_stack_step": (_S, [_P, C.POINTER(StackStepDesc), _P, C.c_size_t, _P]),
     "lak_trace_decode": (_S, [_P, _P, _P]),
     "lak_last_error": (C.c_char_p, []),
 }

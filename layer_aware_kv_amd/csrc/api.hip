@@ -577,6 +577,60 @@ lak_status lak_attn_sparse(lak_cache* c, int32_t layer, const void* q, const voi
                        sel_rows, ws, static_cast<hipStream_t>(stream));
 }
 
+lak_status lak_stack_step(lak_cache* c, const lak_stack_step_desc* st, void* ws, size_t ws_bytes, void* stream) {
+  lak_status s = check_cache(c, true);
+  if (s != LAK_OK) return s;
+  if (!st) return fail(LAK_EINVAL, "step description is NULL");
+  const int L = st->num_layers;
+  if (L <= 0 || L > c->d.num_layers) return fail(LAK_EINVAL, "num_layers %d outside [1, %d]", L, c->d.num_layers);
+  if (!st->tiers || !st->q || !st->k_new || !st->v_new || !st->out || !st->lse || !st->sel || !st->sel_count)
+    return fail(LAK_EINVAL, "a per-layer array is NULL");
+  if (st->agg != LAK_AGG_MAX && st->agg != LAK_AGG_SUM) return fail(LAK_EINVAL, "bad agg %d", st->agg);
+  if ((s = check_ws(c, ws, ws_bytes)) != LAK_OK) return s;
+  bool have_sel = false;
+  for (int l = 0; l < L; ++l) {
+    const int t = st->tiers[l];
+    if (t < 0 || t > 2) return fail(LAK_EINVAL, "layer %d: bad tier %d", l, t);
+    if ((s = check_layer(c, l)) != LAK_OK) return s;
+    if (c->batch > 0 && (!st->q[l] || !st->out[l] || !st->k_new[l] || !st->v_new[l]))
+      return fail(LAK_EINVAL, "layer %d: q / out / k_new / v_new is NULL", l);
+    if (t == MODE_DELTA) {
+      if ((s = check_select_args(c, st->scope, st->k_top, st->recency, st->sel[l], st->sel_count[l],
+                                 st->sel_capacity)) != LAK_OK)
+        return fail(s, "layer %d: %s", l, g_err.c_str());
+      have_sel = true;
+    }
+    if (t == MODE_SPARSE && !have_sel) return fail(LAK_EINVAL, "sparse layer %d comes before any delta-layer", l);
+  }
+  if ((s = lak_step_begin(c, stream)) != LAK_OK) return s;
+  int cur = -1;
+  const hipEvent_t tb0 = c->trace_before, ta0 = c->trace_after;
+  for (int l = 0; l < L; ++l) {
+    const int t = st->tiers[l];
+    if (st->trace_before && st->trace_after) {
+      c->trace_before = static_cast<hipEvent_t>(st->trace_before[l]);
+      c->trace_after = static_cast<hipEvent_t>(st->trace_after[l]);
+      if (!c->trace_before || !c->trace_after) c->trace_before = c->trace_after = nullptr;
+    }
+    if (t == MODE_FULL) {
+      s = lak_attn_full(c, l, st->q[l], st->k_new[l], st->v_new[l], st->sm_scale, st->out[l], st->lse[l], ws,
+                        ws_bytes, stream);
+    } else if (t == MODE_DELTA) {
+      s = lak_attn_delta_select(c, l, st->q[l], st->k_new[l], st->v_new[l], st->sm_scale, st->out[l], st->lse[l],
+                                st->k_top, st->recency, st->agg, st->scope, st->sel[l], st->sel_count[l],
+                                st->sel_capacity, nullptr, ws, ws_bytes, stream);
+      cur = l;
+    } else {
+      s = lak_attn_sparse(c, l, st->q[l], st->k_new[l], st->v_new[l], st->sm_scale, st->sel[cur], st->sel_count[cur],
+                          st->sel_capacity, st->scope, st->out[l], st->lse[l], ws, ws_bytes, stream);
+    }
+    if (s != LAK_OK) break;
+  }
+  c->trace_before = tb0;
+  c->trace_after = ta0;
+  return s == LAK_OK ? ok() : s;
+}
+
 lak_status lak_trace_decode(lak_cache* c, void* before, void* after) {
   if (!c) return fail(LAK_EINVAL, "cache is NULL");
   if ((before == nullptr) != (after == nullptr)) return fail(LAK_EINVAL, "set both trace events or neither");

@@ -8,9 +8,12 @@ first delta-layer.
 """
 from __future__ import annotations
 
+import ctypes as C
+
 import torch
 
-from .cache import PagedKVCache
+from . import _lib as L
+from .cache import PagedKVCache, _AGG, _SCOPE, _stream
 
 
 def layer_tiers(num_layers, full_layers, delta_layers):
@@ -34,7 +37,7 @@ class DeltaStack:
     """
 
     def __init__(self, cache: PagedKVCache, tiers, k_top, recency, sm_scale, agg="max", scope="group",
-                 fused_append=True):
+                 fused_append=True, native=True):
         if tiers and tiers[0] == "sparse":
             raise ValueError("a stack cannot start with a sparse layer")
         first_delta = next((i for i, t in enumerate(tiers) if t == "delta"), None)
@@ -55,6 +58,32 @@ class DeltaStack:
                     for l, t in enumerate(tiers) if t == "delta"}
         self.sel_count = {l: torch.zeros((B, R), dtype=torch.int32, device=dev)
                           for l, t in enumerate(tiers) if t == "delta"}
+        # native path: the whole step is one lak_stack_step call (schedule in C++)
+        self.native = native
+        self._desc = None
+
+    def _native_desc(self):
+        c, L_ = self.c, len(self.tiers)
+        B = c.batch
+        codes = {"full": 0, "delta": 1, "sparse": 2}
+        arr = lambda vals: (C.c_void_p * L_)(*vals)
+        d = L.StackStepDesc()
+        d.num_layers = L_
+        self._tiers = (C.c_int32 * L_)(*[codes[t] for t in self.tiers])
+        self._q, self._kn, self._vn = arr([None] * L_), arr([None] * L_), arr([None] * L_)
+        self._out = arr([self.out[l, :B].data_ptr() for l in range(L_)])
+        self._lse = arr([self.lse[l, :B].data_ptr() for l in range(L_)])
+        self._sel = arr([self.sel[l].data_ptr() if l in self.sel else None for l in range(L_)])
+        self._cnt = arr([self.sel_count[l].data_ptr() if l in self.sel else None for l in range(L_)])
+        d.tiers = C.cast(self._tiers, C.POINTER(C.c_int32))
+        for name, a in (("q", self._q), ("k_new", self._kn), ("v_new", self._vn), ("out", self._out),
+                        ("lse", self._lse), ("sel", self._sel), ("sel_count", self._cnt)):
+            setattr(d, name, C.cast(a, C.POINTER(C.c_void_p)))
+        d.sel_capacity = self.k_top + self.recency
+        d.sm_scale = self.sm_scale
+        d.k_top, d.recency = self.k_top, self.recency
+        d.agg, d.scope = _AGG[self.agg], _SCOPE[self.scope]
+        return d
 
     def step(self, q, k_new, v_new, tracer=None):
         """One decode step.  q [L][B][Hq][D]; k_new, v_new [L][B][Hkv][D] (cache dtype).
@@ -64,6 +93,24 @@ class DeltaStack:
         """
         c = self.c
         B = c.batch
+        if self.native and self.fused_append:
+            if self._desc is None:
+                self._desc = self._native_desc()
+            d = self._desc
+            for l in range(len(self.tiers)):
+                self._q[l], self._kn[l], self._vn[l] = q[l].data_ptr(), k_new[l].data_ptr(), v_new[l].data_ptr()
+            if tracer is not None:
+                n = len(self.tiers)
+                evs = [tracer.pair(l, t) for l, t in enumerate(self.tiers)]
+                self._tb = (C.c_void_p * n)(*[e[0].cuda_event if e else None for e in evs])
+                self._ta = (C.c_void_p * n)(*[e[1].cuda_event if e else None for e in evs])
+                d.trace_before = C.cast(self._tb, C.POINTER(C.c_void_p))
+                d.trace_after = C.cast(self._ta, C.POINTER(C.c_void_p))
+            else:
+                d.trace_before = d.trace_after = None
+            L.check(L.lib().lak_stack_step(c._h, C.byref(d), C.c_void_p(c.ws.data_ptr()), c.ws.numel(), _stream()),
+                    "lak_stack_step")
+            return
         c.step_begin()
         cur = None
         for layer, tier in enumerate(self.tiers):

@@ -130,6 +130,7 @@ def test_attention_calls_on_metadata_only_cache_fail_cleanly():
     assert lib.lak_kv_append(h, 0, dummy, dummy, None) == L.LAK_ESTATE
     assert lib.lak_attn_full(None, 0, dummy, None, None, 1.0, dummy, None, dummy, 1 << 20, None) == L.LAK_EINVAL
     assert lib.lak_workspace_bytes(h) > 0
+    assert lib.lak_stack_step(h, None, dummy, 1 << 20, None) == L.LAK_ESTATE
     lib.lak_cache_destroy(h)
 
 

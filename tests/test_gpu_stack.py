@@ -80,3 +80,47 @@ def test_stack_full_size_sampled(index):
                 assert_close(got_lse, ref_lse, LSE_TOL[wl.dtype], what + " lse")
                 del K, V
     print(f"{wl.name}: {n_band} selected pages differ inside the boundary band", flush=True)
+
+
+def test_native_stack_step_equals_python_loop():
+    """lak_stack_step (schedule in C++) gives the same bits as the per-layer calls."""
+    from layer_aware_kv_amd import DeltaStack, LakError, PagedKVCache
+    from workload.cases import random_case
+    L, B, HQ, HKV, D, P = 6, 3, 8, 2, 64, 16
+    lens = [300, 517, 64]
+    tiers = ["full", "full", "delta", "sparse", "delta", "sparse"]
+    steps = 5
+    runs = []
+    for native in (True, False):
+        cache = PagedKVCache(L, B, HQ, HKV, D, P, 64, 3 * 64, "bf16")
+        cache.seq_reset(lens, reserve_tokens=steps)
+        for layer in range(L):
+            c = random_case(100 + layer, B, HQ, HKV, D, lens, "bf16")
+            cache.kv_prefill(layer, torch.from_numpy(c.K).to(torch.bfloat16).cuda(),
+                             torch.from_numpy(c.V).to(torch.bfloat16).cuda())
+        st = DeltaStack(cache, tiers, 3, 2, 0.125, native=native)
+        outs = []
+        for s in range(steps):
+            c = random_case(200 + s, L * B, HQ, HKV, D, [1], "bf16")
+            q = torch.from_numpy(c.q).to(torch.bfloat16).cuda().view(L, B, HQ, D)
+            kn = torch.from_numpy(c.k_new).to(torch.bfloat16).cuda().view(L, B, HKV, D)
+            vn = torch.from_numpy(c.v_new).to(torch.bfloat16).cuda().view(L, B, HKV, D)
+            st.step(q, kn, vn)
+            outs.append((st.out.clone(), st.lse.clone(), {l: v.clone() for l, v in st.sel.items()}))
+        torch.cuda.synchronize()
+        runs.append(outs)
+    for (o1, l1, s1), (o2, l2, s2) in zip(*runs):
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        assert all(torch.equal(s1[k], s2[k]) for k in s1)
+    # a sparse layer before any delta-layer is refused before anything runs
+    cache = PagedKVCache(2, 1, 4, 1, 64, 16, 8, 8, "bf16")
+    cache.seq_reset([20], reserve_tokens=4)
+    st = DeltaStack.__new__(DeltaStack)
+    DeltaStack.__init__(st, cache, ["full", "delta"], 1, 1, 1.0)
+    st.tiers = ["full", "sparse"]
+    st._desc = None
+    z = torch.zeros((2, 1, 4, 64), dtype=torch.bfloat16, device="cuda")
+    zk = torch.zeros((2, 1, 1, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(LakError, match="LAK_EINVAL"):
+        st.step(z, zk, zk)
+    assert cache.seq_lens_host() == [20]  # nothing ran, not even the step's length increment
