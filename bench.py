@@ -177,7 +177,19 @@ def main():
     ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1, help="batch rows in the CPU oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes three times (for HBM counter scaling)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "dispatches": 3}))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -311,12 +323,43 @@ def main():
         "stack_GBps": round(total_step_bytes / (tA / K) / 1e9, 1),
         "device": props.name,
     }
+    # D: selection fidelity (untimed): at sampled steps every sparse layer is also run
+    # with full attention on the same query; recall = exp(lse_sparse - lse_full)
+    result["fidelity"] = fidelity_pass(sb, torch)
+    log("fidelity: recall mean {recall_mean}, p05 {recall_p05}, min {recall_min}; max |out err| "
+        "{max_abs_out_err}".format(**result["fidelity"]))
     del sb
     torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, rec, tiers, W, args.cpu_rows)
     print(json.dumps(result), flush=True)
+
+
+def fidelity_pass(sb, torch):
+    """Attention-mass recall of the selections and sparse-vs-full output error, per
+    sparse layer, at the first and last timed steps and around drift events."""
+    from layer_aware_kv_amd import fidelity
+    wl, cache = sb.wl, sb.cache
+    sample = {sb.W, sb.S - 1}
+    for s in sb.drift:
+        sample |= {s - 1, s}
+    sample = {s for s in sample if 0 <= s < sb.S}
+    sparse = [l for l, t in enumerate(sb.tiers) if t == "sparse"]
+    recalls, errors = {}, {}
+
+    def on_step(s, stack):
+        if s not in sample:
+            return
+        B = cache.batch
+        for layer in sparse:
+            out_f, lse_f = cache.attn_full(layer, sb.Q[s][layer], wl.sm_scale)
+            recalls[(s, layer)] = fidelity.selection_recall(stack.lse[layer, :B], lse_f)
+            errors[(s, layer)] = (stack.out[layer, :B].float() - out_f.float()).abs().amax(dim=-1)
+
+    sb.run(sb.tiers, on_step=on_step)
+    torch.cuda.synchronize()
+    return fidelity.summarize(recalls, errors)
 
 
 def cpu_baseline(wl, rec, tiers, step, rows, repeats=3):

@@ -305,3 +305,23 @@ def test_fused_append_matches_separate_append(spec):
             for g in range(case.K.shape[1]):
                 kg, vg = cache_b.kv_gather(0, b, g, case.lengths[b] - 1, 1)
                 assert torch.equal(kg[0], kn[b, g]) and torch.equal(vg[0], vn[b, g])
+
+
+def test_fidelity_recall_matches_oracle_mass():
+    """The device recall exp(lse_sparse - lse_full) equals the oracle's full-softmax
+    mass of the selected tokens."""
+    from layer_aware_kv_amd import fidelity
+    from oracle.attention import selected_tokens
+    case, P, sm = _case(CASES[2])
+    cache = make_cache(case, P)
+    q = fill_and_step(cache, case)
+    out_f, lse_f = cache.attn_full(0, q, sm)
+    _, _, sel, cnt = cache.attn_delta_select(0, q, sm, 12, 2)
+    _, lse_s = cache.attn_sparse(0, q, sm, sel, cnt)
+    rec = fidelity.selection_recall(lse_s, lse_f).cpu().numpy()
+    G = case.q.shape[1] // case.K.shape[1]
+    for b, T in enumerate(case.lengths):
+        _, _, p = oracle.full_attention(case.q[b], case.K[b, :, :T], case.V[b, :, :T], sm)
+        for h in range(case.q.shape[1]):
+            toks = selected_tokens(sel[b, h // G, :int(cnt[b, h // G])].cpu().tolist(), T, P)
+            assert abs(rec[b, h] - p[h, toks].sum()) < 5e-3

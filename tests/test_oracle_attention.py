@@ -105,3 +105,18 @@ def test_selected_tokens_masks_partial_page():
     from oracle.attention import selected_tokens
     assert selected_tokens([0, 2], 40, 16).tolist() == list(range(16)) + list(range(32, 40))
     assert selected_tokens([], 40, 16).size == 0
+
+
+def test_selection_mass_identity():
+    """Attention mass of the selected tokens under the full softmax equals
+    exp(lse_sparse - lse_full): the recall measure of the fidelity study."""
+    rng = np.random.default_rng(21)
+    hq, hkv, T, D, page = 8, 2, 300, 32, 16
+    q, K, V = _rand(rng, hq, hkv, T, D)
+    sel = [[0, 4, 7, 18], [2, 3, 18]]
+    _, lse_f, p = oracle.full_attention(q, K, V, 0.3)
+    _, lse_s = oracle.sparse_attention(q, K, V, sel, page, 0.3)
+    from oracle.attention import selected_tokens
+    for h in range(hq):
+        toks = selected_tokens(sel[h // 4], T, page)
+        assert abs(p[h, toks].sum() - np.exp(lse_s[h] - lse_f[h])) < 1e-12
