@@ -39,6 +39,7 @@ lak_status hip_fail(hipError_t e, const char* where) {
 // LAK_TUNE_TARGET_WGS overrides) and the fewest 16-token sub-tiles one workgroup
 // is given.
 constexpr int kTargetWgs = 1024;
+constexpr int kTargetWgsDelta = 4096;  // smaller delta splits spread the logits writes
 constexpr int kMinSubtilesPerWg = 8;
 // Each of the 4 waves of a decode workgroup keeps the page ids of its items in one
 // register per lane, so a split holds at most 4 * 64 items.
@@ -67,7 +68,13 @@ int lak::tune_decode_batch(int mode) {
 int lak::tune_target_wgs(int mode) {
   static const int full = env_int("LAK_TUNE_TARGET_WGS", kTargetWgs, 64, 65536);
   static const int sparse = env_int("LAK_TUNE_SPARSE_WGS", kTargetWgs, 64, 65536);
-  return mode == MODE_SPARSE ? sparse : full;
+  static const int delta = env_int("LAK_TUNE_DELTA_WGS", kTargetWgsDelta, 64, 65536);
+  return mode == MODE_SPARSE ? sparse : (mode == MODE_DELTA ? delta : full);
+}
+
+int lak::tune_delta_lds() {
+  static const int v = env_int("LAK_TUNE_DELTA_LDS", 1, 0, 1);
+  return v;
 }
 
 struct lak_cache {
@@ -112,10 +119,12 @@ WsLayout ws_layout(const lak_cache* c) {
   WsLayout w;
   size_t off = 0;
   const size_t rows_h = (size_t)d.max_batch * d.num_q_heads;
+  // split partials are [B][Hq][S] with S the call's split count: B * S <= s_cap
+  const size_t part = (size_t)d.num_q_heads * c->s_cap;
   w.o_part = off;
-  off = align256(off + rows_h * c->s_cap * d.head_dim * sizeof(float));
+  off = align256(off + part * d.head_dim * sizeof(float));
   w.ml_part = off;
-  off = align256(off + rows_h * c->s_cap * 2 * sizeof(float));
+  off = align256(off + part * 2 * sizeof(float));
   w.lse = off;
   off = align256(off + rows_h * sizeof(float));
   w.logits = off;  // [B][Hkv][sub-tiles][Gp][16], Gp = G rounded up to even
@@ -184,7 +193,8 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
   const int rows = c->batch * d.num_kv_heads;
   const int pps = plan_pps(rows, max_items, spp, mode);
   const int splits = (max_items + pps - 1) / pps;
-  if (splits > c->s_cap) return fail(LAK_EINVAL, "internal: %d splits exceed capacity %d", splits, c->s_cap);
+  if ((int64_t)splits * c->batch > c->s_cap)
+    return fail(LAK_EINVAL, "internal: %d splits x %d rows exceed capacity %d", splits, c->batch, c->s_cap);
 
   DecodeArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -201,7 +211,7 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
   a.page = d.page_size;
   a.max_pages = d.max_pages_per_seq;
   a.pps = pps;
-  a.s_cap = c->s_cap;
+  a.s_cap = splits;
   a.sel = sel;
   a.sel_count = sel_count;
   a.sel_cap = sel_cap;
@@ -209,6 +219,11 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
   a.o_part = reinterpret_cast<float*>(wsb + w.o_part);
   a.ml_part = reinterpret_cast<float*>(wsb + w.ml_part);
   a.logits = reinterpret_cast<float*>(wsb + w.logits);
+  {
+    const int G = d.num_q_heads / d.num_kv_heads;
+    const size_t staged = (size_t)pps * (d.page_size / 16) * (G + (G & 1)) * 16 * sizeof(float);
+    a.lds_logits = (mode == MODE_DELTA && tune_delta_lds() && staged <= 64 * 1024) ? 1 : 0;
+  }
   a.t_pad = (int64_t)d.max_pages_per_seq * d.page_size;
   hipError_t e = hipSuccess;
   if (c->trace_before) e = hipEventRecord(c->trace_before, st);
@@ -228,7 +243,7 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
   cb.hkv = d.num_kv_heads;
   cb.page = d.page_size;
   cb.pps = pps;
-  cb.s_cap = c->s_cap;
+  cb.s_cap = splits;
   cb.splits = splits;
   cb.out = out;
   cb.lse = lse;
@@ -315,10 +330,15 @@ lak_status lak_cache_create(const lak_cache_desc* desc, lak_cache** out) {
   c->pages.resize(d.max_batch);
   c->lens.assign(d.max_batch, 0);
   c->reset_free_list();
-  c->s_cap = std::min(std::max((std::max(tune_target_wgs(MODE_FULL), tune_target_wgs(MODE_SPARSE)) +
-                                d.num_kv_heads - 1) / d.num_kv_heads,
-                               (d.max_pages_per_seq + kMaxItemsPerSplit - 1) / kMaxItemsPerSplit),
-                      d.max_pages_per_seq);
+  // Bound on B * S over all calls: with pps >= ceil(R * M / target) (R = B * Hkv rows of
+  // at most M items) S <= target / R + 1, and with pps capped at kMaxItemsPerSplit
+  // S <= M / kMaxItemsPerSplit + 1.
+  {
+    const int tmax = std::max(std::max(tune_target_wgs(MODE_FULL), tune_target_wgs(MODE_SPARSE)),
+                              tune_target_wgs(MODE_DELTA));
+    c->s_cap = (tmax + d.num_kv_heads - 1) / d.num_kv_heads +
+               d.max_batch * ((d.max_pages_per_seq + kMaxItemsPerSplit - 1) / kMaxItemsPerSplit + 2);
+  }
   *out = c;
   return ok();
 }

@@ -14,6 +14,8 @@
 // partials (o, max, sum) are merged by combine_kernel.
 #include <math.h>
 
+#include <algorithm>
+
 #include "lak_device.h"
 #include "lak_internal.h"
 
@@ -292,7 +294,7 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
 #pragma unroll
   for (int x = 0; x < F::NO; ++x) o[x] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  auto process = [&](F& f, int ct) {
+  auto process = [&](F& f, int ct, int x) {
     if (krow_new != nullptr && T - 1 < ct + kSub) f.patch(krow_new, vrow_new, (T - 1) - ct, lane);
     const f32x4 sacc = f.qk(qf);
     const int tb = ct + 4 * j;
@@ -311,8 +313,14 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
       f32x4 w;
 #pragma unroll
       for (int r = 0; r < 4; ++r) w[r] = (head_ok && tb + r < T) ? sacc[r] * a.sm_scale : -INFINITY;
-      const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + ct / kSub;
-      *reinterpret_cast<f32x4*>(a.logits + (blk * Gp + n) * kSub + 4 * j) = w;
+      if (a.lds_logits) {
+        // staged in LDS at the sub-tile's index within the workgroup; flushed at the end
+        const int li = (wave + kWaves * (x / spp)) * spp + (x % spp);
+        *reinterpret_cast<f32x4*>(lds + (li * Gp + n) * kSub + 4 * j) = w;
+      } else {
+        const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + ct / kSub;
+        *reinterpret_cast<f32x4*>(a.logits + (blk * Gp + n) * kSub + 4 * j) = w;
+      }
     }
     mx = fmaxf(mx, shfl_xor_f(mx, 16));
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
@@ -346,7 +354,26 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (info[u].valid) process(buf[u], info[u].t0);
+      if (info[u].valid) process(buf[u], info[u].t0, x + u);
+  }
+
+  if (MODE == MODE_DELTA && a.lds_logits) {
+    // write the workgroup's logits blocks in one burst (whole 16-byte units per thread)
+    __syncthreads();
+    const int n_units = n_split * spp * Gp * 4;
+    for (int idx = threadIdx.x; idx < n_units; idx += blockDim.x) {
+      const int q4 = idx & 3;
+      const int hn = (idx >> 2) % Gp;
+      const int li = (idx >> 2) / Gp;
+      const int member = li / spp, sub = li - member * spp;
+      const int t0 = (s + S_row * member) * P + sub * kSub;
+      if (t0 < T) {
+        const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + t0 / kSub;
+        *reinterpret_cast<f32x4*>(a.logits + (blk * Gp + hn) * kSub + 4 * q4) =
+            *reinterpret_cast<const f32x4*>(lds + (li * Gp + hn) * kSub + 4 * q4);
+      }
+    }
+    __syncthreads();  // the merge below reuses this LDS
   }
 
   l += shfl_xor_f(l, 16);
@@ -478,7 +505,9 @@ template <int ESZ, int D>
 static hipError_t launch_decode_t(int mode, const DecodeArgs& a, int splits, int batch,
                                   hipStream_t st) {
   const int G = a.hq / a.hkv;
-  const size_t lds = (size_t)(kWaves * G * D + 2 * kWaves * 16) * sizeof(float);
+  size_t lds = (size_t)(kWaves * G * D + 2 * kWaves * 16) * sizeof(float);
+  if (mode == MODE_DELTA && a.lds_logits)
+    lds = std::max(lds, (size_t)a.pps * (a.page / kSub) * (G + (G & 1)) * kSub * sizeof(float));
   dim3 grid(splits, a.hkv, batch);
   const int u = tune_decode_batch(mode);
   if (u == 4)

@@ -20,7 +20,7 @@ struct DecodeArgs {
   float sm_scale;
   int hq, hkv, page, max_pages;
   int pps;                     // items (pages or selection entries) per split
-  int s_cap;                   // split stride of the partial buffers
+  int s_cap;                   // split stride of the partial buffers (= splits launched)
   // sparse tier
   const int32_t* sel;          // [B][R][sel_cap]
   const int32_t* sel_count;    // [B][R]
@@ -30,6 +30,7 @@ struct DecodeArgs {
   float* o_part;               // [B][Hq][s_cap][D]
   float* ml_part;              // [B][Hq][s_cap][2]  (max in log2 units, sum)
   float* logits;               // delta tier: [B][Hkv][t_pad/16][Gp][16] (Gp = G rounded up to even)
+  int lds_logits;              // delta tier: stage logits in LDS and write them at the split's end
   int64_t t_pad;               // token capacity of a sequence (max_pages * page)
 };
 
@@ -85,8 +86,11 @@ struct KvGeom {
 //   LAK_TUNE_SPARSE_BATCH  the same for the sparse tier (1, 2 or 4)
 //   LAK_TUNE_TARGET_WGS    workgroups a full / delta split-K launch aims for
 //   LAK_TUNE_SPARSE_WGS    workgroups a sparse split-K launch aims for
+//   LAK_TUNE_DELTA_WGS     workgroups a delta split-K launch aims for
+//   LAK_TUNE_DELTA_LDS     1 (default): delta logits staged in LDS, written at a split's end
 int tune_decode_batch(int mode);
 int tune_target_wgs(int mode);
+int tune_delta_lds();
 
 // launchers (return hipSuccess or the launch error)
 hipError_t launch_decode(int dtype, int mode, int D, const DecodeArgs& a, int splits, int batch,
