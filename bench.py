@@ -85,7 +85,7 @@ class Tracer:
 class StackBench:
     """Device set-up and the step loop of one stack workload (inputs resident in HBM)."""
 
-    def __init__(self, wl, warmup, steps):
+    def __init__(self, wl, warmup, steps, agg="max", scope="group"):
         import torch
         from layer_aware_kv_amd import PagedKVCache, layer_tiers
         from workload import Recipe
@@ -93,6 +93,7 @@ class StackBench:
 
         self.torch = torch
         self.wl = wl
+        self.agg, self.scope = agg, scope
         self.W, self.K = warmup, steps
         self.S = warmup + steps
         self.rec = Recipe(wl)
@@ -145,7 +146,7 @@ class StackBench:
         cache.seq_reset(self.lens0, reserve_tokens=self.S)
         if self.dirty:  # a drift event rewrote keys: restore the prefilled state
             self.prefill_all()
-        stack = DeltaStack(cache, tiers, wl.k_top, wl.recency, wl.sm_scale)
+        stack = DeltaStack(cache, tiers, wl.k_top, wl.recency, wl.sm_scale, self.agg, self.scope)
 
         def one(s, tr):
             if s in self.drift:
@@ -177,6 +178,12 @@ def main():
     ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1, help="batch rows in the CPU oracle sample")
+    ap.add_argument("--agg", choices=["max", "sum"], default="max",
+                    help="head aggregation of the delta-layers (max: the pages' rule)")
+    ap.add_argument("--scope", choices=["group", "all"], default="group",
+                    help="heads aggregated per selection: each KV group, or all query heads")
+    ap.add_argument("--delta-layers", default=None,
+                    help="comma-separated delta-layer list replacing the workload's (sweeps)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (for HBM counter scaling)")
     args = ap.parse_args()
@@ -202,6 +209,9 @@ def main():
     from workload import CONFIGS
 
     wl = CONFIGS[args.config]
+    if args.delta_layers is not None:
+        import dataclasses
+        wl = dataclasses.replace(wl, delta_layers=tuple(int(x) for x in args.delta_layers.split(",") if x != ""))
     W = wl.warmup if args.warmup is None else args.warmup
     K = wl.steps if args.steps is None else args.steps
     B, L, HQ, HKV, D, P = wl.batch, wl.num_layers, wl.hq, wl.hkv, wl.d, wl.page
@@ -211,7 +221,7 @@ def main():
     log(f"device {props.name} ({props.multi_processor_count} CUs), workload {wl.name}, W={W} K={K}")
 
     t_setup = time.perf_counter()
-    sb = StackBench(wl, W, K)
+    sb = StackBench(wl, W, K, agg=args.agg, scope=args.scope)
     lens0, tiers, rec = sb.lens0, sb.tiers, sb.rec
     log(f"set-up {time.perf_counter() - t_setup:.1f} s: {2 * L * sb.cache.k_pools[0].numel() * e / 1e9:.1f} GB "
         f"of KV pools; drift events at steps {sorted(sb.drift)}")
@@ -299,7 +309,7 @@ def main():
             "layers": L, "batch": B, "context": wl.context, "q_heads": HQ, "kv_heads": HKV, "head_dim": D,
             "page": P, "top_k_pages": wl.k_top, "recency_pages": wl.recency,
             "full_layers": list(wl.full_layers), "delta_layers": list(wl.delta_layers),
-            "ragged_min": wl.ragged_min, "parallelism": "single GPU",
+            "ragged_min": wl.ragged_min, "agg": args.agg, "scope": args.scope, "parallelism": "single GPU",
         },
         "roofline": {
             "bound": "hbm",

@@ -183,7 +183,8 @@ lak_status check_ws(const lak_cache* c, const void* ws, size_t ws_bytes) {
 // Runs the split-K decode plus combine of one tier.
 lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const void* k_new,
                          const void* v_new, float sm_scale, void* out, float* lse, const int32_t* sel,
-                         const int32_t* sel_count, int sel_cap, int sel_rows, void* ws, hipStream_t st) {
+                         const int32_t* sel_count, int sel_cap, int sel_rows, void* ws, hipStream_t st,
+                         int agg = LAK_AGG_MAX) {
   const auto& d = c->d;
   const WsLayout w = ws_layout(c);
   char* wsb = static_cast<char*>(ws);
@@ -223,6 +224,7 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
     const int G = d.num_q_heads / d.num_kv_heads;
     const size_t staged = (size_t)pps * (d.page_size / 16) * (G + (G & 1)) * 16 * sizeof(float);
     a.lds_logits = (mode == MODE_DELTA && tune_delta_lds() && staged <= 64 * 1024) ? 1 : 0;
+    a.sum_pairs = (mode == MODE_DELTA && agg == LAK_AGG_SUM) ? 1 : 0;
   }
   a.t_pad = (int64_t)d.max_pages_per_seq * d.page_size;
   hipError_t e = hipSuccess;
@@ -545,7 +547,7 @@ lak_status lak_attn_delta_select(lak_cache* c, int32_t layer, const void* q, con
   if (c->batch == 0) return ok();
   if ((s = check_ws(c, ws, ws_bytes)) != LAK_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  s = run_attention(c, layer, MODE_DELTA, q, k_new, v_new, sm_scale, out, lse, nullptr, nullptr, 0, 1, ws, st);
+  s = run_attention(c, layer, MODE_DELTA, q, k_new, v_new, sm_scale, out, lse, nullptr, nullptr, 0, 1, ws, st, agg);
   if (s != LAK_OK) return s;
   const WsLayout w = ws_layout(c);
   char* wsb = static_cast<char*>(ws);
@@ -564,7 +566,8 @@ lak_status lak_attn_delta_select(lak_cache* c, int32_t layer, const void* q, con
   pa.scope = scope;
   pa.tokens_per_block = kScoreTokensPerBlock;
   const int rows = scope == LAK_SCOPE_GROUP ? c->d.num_kv_heads : 1;
-  hipError_t e = launch_page_score(pa, c->batch, rows, c->max_np(), st);
+  hipError_t e = (agg == LAK_AGG_SUM) ? launch_page_score_pairs(pa, c->batch, rows, c->max_np(), st)
+                                      : launch_page_score(pa, c->batch, rows, c->max_np(), st);
   if (e != hipSuccess) return hip_fail(e, "page score launch");
   return run_select(c, scores, scope, k_top, recency, sel, sel_count, sel_capacity, st);
 }

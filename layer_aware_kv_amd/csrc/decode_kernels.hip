@@ -305,7 +305,22 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
       s2[r] = (tb + r < T) ? sacc[r] * qk_scale2 : -INFINITY;
       mx = fmaxf(mx, s2[r]);
     }
-    if (MODE == MODE_DELTA && n < Gp) {
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    if (MODE == MODE_DELTA && a.sum_pairs) {
+      // (r, e) of this head over the sub-tile: r = max logit (log2 units), e = sum of
+      // 2^(logit - r); the page score later is sum_h e * exp(r ln 2 - lse_h)
+      float e = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) e += exp2f(s2[r] - mx);
+      e += shfl_xor_f(e, 16);
+      e += shfl_xor_f(e, 32);
+      if (head_ok && j == 0) {
+        const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + ct / kSub;
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<f32x2*>(a.logits + (blk * Gp + n) * 2) = (f32x2){mx, e};
+      }
+    } else if (MODE == MODE_DELTA && n < Gp) {
       // Logits block of (b, g, sub-tile): [Gp heads][16 tokens], Gp = G rounded up to
       // even, so one store instruction writes whole 128-byte lines (the padding head,
       // if any, is written too).  Plain stores: the block stays cache-resident for the
@@ -322,8 +337,6 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
         *reinterpret_cast<f32x4*>(a.logits + (blk * Gp + n) * kSub + 4 * j) = w;
       }
     }
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
     const float m_new = fmaxf(m2, mx);
     const float alpha = exp2f(m2 - m_new);
     float p[4];
@@ -357,7 +370,7 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
       if (info[u].valid) process(buf[u], info[u].t0, x + u);
   }
 
-  if (MODE == MODE_DELTA && a.lds_logits) {
+  if (MODE == MODE_DELTA && a.lds_logits && !a.sum_pairs) {
     // write the workgroup's logits blocks in one burst (whole 16-byte units per thread)
     __syncthreads();
     const int n_units = n_split * spp * Gp * 4;
@@ -506,7 +519,7 @@ static hipError_t launch_decode_t(int mode, const DecodeArgs& a, int splits, int
                                   hipStream_t st) {
   const int G = a.hq / a.hkv;
   size_t lds = (size_t)(kWaves * G * D + 2 * kWaves * 16) * sizeof(float);
-  if (mode == MODE_DELTA && a.lds_logits)
+  if (mode == MODE_DELTA && a.lds_logits && !a.sum_pairs)
     lds = std::max(lds, (size_t)a.pps * (a.page / kSub) * (G + (G & 1)) * kSub * sizeof(float));
   dim3 grid(splits, a.hkv, batch);
   const int u = tune_decode_batch(mode);

@@ -31,6 +31,8 @@ struct DecodeArgs {
   float* ml_part;              // [B][Hq][s_cap][2]  (max in log2 units, sum)
   float* logits;               // delta tier: [B][Hkv][t_pad/16][Gp][16] (Gp = G rounded up to even)
   int lds_logits;              // delta tier: stage logits in LDS and write them at the split's end
+  int sum_pairs;               // delta tier with SUM aggregation: write per (head, sub-tile) the
+                               // pair (max logit in log2 units, sum of 2^(logit - max)) instead of logits
   int64_t t_pad;               // token capacity of a sequence (max_pages * page)
 };
 
@@ -58,6 +60,9 @@ struct PageScoreArgs {
   int scope;                  // 0 group, 1 all
   int tokens_per_block;
 };
+
+// SUM aggregation from the decode kernel's (max, sum) pairs: no logits needed.
+hipError_t launch_page_score_pairs(const PageScoreArgs& a, int batch, int rows, int max_np, hipStream_t st);
 
 struct TopkArgs {
   const float* scores;        // [B][R][max_pages]

@@ -84,6 +84,43 @@ hipError_t launch_page_score(const PageScoreArgs& a, int batch, int rows, int ma
   return hipGetLastError();
 }
 
+// SUM aggregation without logits: one thread per page adds, over the scope's KV
+// heads, the page's sub-tiles and the group's heads, e * exp(r ln 2 - lse_h) from the
+// (r, e) pairs the delta decode kernel wrote per (b, g, sub-tile, head) -- that is
+// sum_t exp(logit_t - lse_h) over the page's valid tokens, exactly.
+__global__ __launch_bounds__(256) void page_score_pairs_kernel(PageScoreArgs a) {
+  const int r = blockIdx.y, b = blockIdx.z;
+  const int jp = blockIdx.x * blockDim.x + threadIdx.x;
+  const int T = a.seq_lens[b];
+  const int NP = min((T + a.page - 1) / a.page, a.max_pages);
+  if (jp >= NP) return;
+  const int G = a.hq / a.hkv;
+  const int Gp = G + (G & 1);
+  const int g_lo = a.scope == 0 ? r : 0;
+  const int g_hi = a.scope == 0 ? r + 1 : a.hkv;
+  const int rows = a.scope == 0 ? a.hkv : 1;
+  const int spp = a.page / 16;
+  const int64_t nsub = a.t_pad / 16;
+  const float* ls = a.lse + (int64_t)b * a.hq;
+  float acc = 0.f;
+  for (int g = g_lo; g < g_hi; ++g) {
+    for (int u = 0; u < spp; ++u) {
+      const int st = jp * spp + u;
+      if (st * 16 >= T) break;
+      const float* pp = a.logits + ((((int64_t)b * a.hkv + g) * nsub + st) * Gp) * 2;
+      for (int h = 0; h < G; ++h) acc += pp[2 * h + 1] * expf(pp[2 * h] * kLn2 - ls[g * G + h]);
+    }
+  }
+  a.scores[((int64_t)b * rows + r) * a.max_pages + jp] = acc;
+}
+
+hipError_t launch_page_score_pairs(const PageScoreArgs& a, int batch, int rows, int max_np, hipStream_t st) {
+  if (batch == 0 || max_np == 0) return hipSuccess;
+  dim3 grid((unsigned)((max_np + 255) / 256), rows, batch);
+  hipLaunchKernelGGL(page_score_pairs_kernel, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 // Order key of a score: float32 bits of a positive score (monotone for x >= 0);
 // zero, negative and NaN scores all map to 0.
 __device__ inline uint32_t score_key(float x) { return (x > 0.f) ? __float_as_uint(x) : 0u; }
