@@ -336,8 +336,9 @@ def main():
     # D: selection fidelity (untimed): at sampled steps every sparse layer is also run
     # with full attention on the same query; recall = exp(lse_sparse - lse_full)
     result["fidelity"] = fidelity_pass(sb, torch)
-    log("fidelity: recall mean {recall_mean}, p05 {recall_p05}, min {recall_min}; max |out err| "
-        "{max_abs_out_err}".format(**result["fidelity"]))
+    if result["fidelity"]:
+        log("fidelity: recall mean {recall_mean}, p05 {recall_p05}, min {recall_min}; max |out err| "
+            "{max_abs_out_err}".format(**result["fidelity"]))
     del sb
     torch.cuda.empty_cache()
 
