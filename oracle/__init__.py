@@ -19,11 +19,18 @@ Everything is plain NumPy in float64, one (batch row, head) at a time, in the
 order the pages state the steps.  Readings of points the pages leave open are
 listed in each function's docstring.
 
+fp8 KV pages (``quant``): OCP E4M3 codes with one float32 scale per (token,
+KV head) row; the pages name quantization as a technique to combine with DELTA
+("Future Directions") and fix no format, so the format and its readings are
+stated in that module.
+
 Pins (tests/test_oracle_*.py): torch's scaled_dot_product_attention in float64,
-scipy's logsumexp, closed forms, brute-force subset search for the selection,
-and the invariants the pages state (no eviction; all delta-layers -> full
-attention).  Parity status of every function: pinned.
+scipy's logsumexp, torch's float8_e4m3fn conversions, closed forms, brute-force
+subset search for the selection, and the invariants the pages state (no
+eviction; all delta-layers -> full attention).  Parity status of every function:
+pinned.
 """
 from .attention import full_attention, sparse_attention, attention_over_tokens  # noqa: F401
 from .delta import token_scores, page_scores, select_pages, delta_layer  # noqa: F401
 from .stack import layer_tiers, stack_step  # noqa: F401
+from . import quant  # noqa: F401

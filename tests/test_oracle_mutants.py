@@ -122,3 +122,45 @@ def test_mutant_stale_selection_caught(monkeypatch):
     monkeypatch.setattr(oracle, "stack_step", stale)
     with pytest.raises(AssertionError):
         TS.test_sparse_layers_use_latest_delta_selection()
+
+
+# ---- fp8 rows (oracle.quant) ----
+import oracle.quant as oq  # noqa: E402
+from tests import test_oracle_quant as TQ  # noqa: E402
+
+
+def test_mutant_e4m3_bias_caught(monkeypatch):
+    real = oq.e4m3_decode
+    monkeypatch.setattr(oq, "e4m3_decode", lambda c: real(c) / 2.0)  # exponent bias 8 instead of 7
+    with pytest.raises(AssertionError):
+        TQ.test_decode_matches_torch_float8_e4m3fn()
+
+
+def test_mutant_ties_away_caught(monkeypatch):
+    pos = oq._POS
+
+    def encode_ties_away(x):
+        x = np.asarray(x, dtype=np.float64)
+        a = np.abs(x)
+        hi = np.clip(np.searchsorted(pos, a, side="left"), 0, len(pos) - 1)
+        lo = np.clip(hi - 1, 0, len(pos) - 1)
+        pick = np.where(np.abs(a - pos[lo]) < np.abs(pos[hi] - a), lo, hi)
+        return (pick | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+    monkeypatch.setattr(oq, "e4m3_encode", encode_ties_away)
+    with pytest.raises(AssertionError):
+        TQ.test_encode_matches_torch_rne_including_ties()
+
+
+def test_mutant_wrong_scale_constant_caught(monkeypatch):
+    real_encode = oq.e4m3_encode
+
+    def quantize_240(x):  # the largest value of the other E4M3 variant
+        x32 = np.asarray(x, dtype=np.float32)
+        scale = (np.max(np.abs(x32), axis=-1) / np.float32(240)).astype(np.float32)
+        safe = np.where(scale > 0, scale, np.float32(1)).astype(np.float32)
+        return real_encode(np.clip(x32 / safe[..., None], -448, 448)), scale
+
+    monkeypatch.setattr(oq, "quantize_rows", quantize_240)
+    with pytest.raises(AssertionError):
+        TQ.test_quantize_rows_exact_on_representable_rows()
