@@ -27,7 +27,7 @@
  *   - T_b (the current length of sequence b) always includes the token appended
  *     in the current decode step; NP_b = ceil(T_b / P) pages.
  *   - Element types: LAK_BF16 (bfloat16, float32 accumulation, outputs rounded to
- *     nearest even) or LAK_F32.
+ *     nearest even), LAK_F32, or LAK_FP8_E4M3 pools (rows in and out bfloat16).
  *   - Calls on one cache are not thread safe; calls that overlap on the device
  *     (different streams, same workspace) race.
  */
@@ -50,7 +50,14 @@ typedef enum {
   LAK_ESTATE = -5        /* call out of order (e.g. no batch set by lak_seq_reset) */
 } lak_status;
 
-typedef enum { LAK_BF16 = 0, LAK_F32 = 1 } lak_dtype;
+/* Pool element types.  LAK_FP8_E4M3: each (token, KV head) row of K and of V is
+ * stored as D OCP E4M3 codes plus one float32 scale (scale = max|x| / 448, code =
+ * round-to-nearest-even of x / scale; a row of zeros has scale 0).  The pages
+ * name quantization as a technique to combine with DELTA ("Future Directions");
+ * the format is the OCP 8-bit floating point E4M3 encoding.  Rows going in
+ * (prefill, append, write_rows, k_new / v_new) and q / out are bfloat16 for such
+ * a cache; attention runs on code * scale with float32 accumulation. */
+typedef enum { LAK_BF16 = 0, LAK_F32 = 1, LAK_FP8_E4M3 = 2 } lak_dtype;
 
 /* Head aggregation of per-token scores in a delta-layer.  MAX is the pages' rule
  * (maximum attention weight across heads); SUM adds the weights instead. */
@@ -89,7 +96,8 @@ typedef struct {
   int32_t* seq_lens;          /* device [max_batch] */
 } lak_cache_desc;
 
-/* Bytes of one K (or V) pool: num_pages * Hkv * P * D * element size; -1 if invalid. */
+/* Bytes of one K (or V) pool: num_pages * Hkv * P * D * element size, plus
+ * num_pages * Hkv * P * 4 for the scales of an fp8 pool; -1 if invalid. */
 int64_t lak_pool_bytes(const lak_cache_desc* desc);
 
 /* Validates `desc` and creates the host metadata.  No HIP call is made.
@@ -147,16 +155,23 @@ lak_status lak_kv_write_rows(lak_cache* cache, int32_t layer, int32_t n, const i
                              const void* k_rows, const void* v_rows, void* stream);
 
 /* Reads tokens [t0, t0 + n) of (b, kv head g) of layer `layer` back in logical order
- * into k_out, v_out: device [n][D] (either may be NULL).  Requires t0 + n <= T_b. */
+ * into k_out, v_out: device [n][D] (either may be NULL) in the pool's element type
+ * (the E4M3 codes, one byte each, for an fp8 pool).  Requires t0 + n <= T_b. */
 lak_status lak_kv_gather(lak_cache* cache, int32_t layer, int32_t b, int32_t g, int32_t t0,
                          int32_t n, void* k_out, void* v_out, void* stream);
+
+/* fp8 pools only: the float32 scales of the same rows into k_out, v_out: device
+ * [n] (either may be NULL).  Errors: EINVAL (not an fp8 cache, range). */
+lak_status lak_kv_gather_scales(lak_cache* cache, int32_t layer, int32_t b, int32_t g, int32_t t0,
+                                int32_t n, float* k_out, float* v_out, void* stream);
 
 /* Full decode attention of layer `layer` (layers 0-1 and delta-layers: "run
  * ordinary full attention"): out[b][h] = sum_t p_t v_t over t < T_b with
  * p = softmax(sm_scale * <q[b][h], k_t>).  Split-K over pages plus a combine kernel.
  * k_new, v_new (both NULL, or both device [B][Hkv][D]): this step's key and value;
  * when given, the call also appends them at position T_b - 1, exactly as
- * lak_kv_append would before the call (one launch fewer).  The same holds for the
+ * lak_kv_append would before the call (one launch fewer; for an fp8 cache the
+ * call enqueues that append kernel itself).  The same holds for the
  * k_new / v_new arguments of lak_attn_delta_select and lak_attn_sparse.
  * lse may be NULL.  ws: lak_workspace_bytes() bytes of device memory. */
 lak_status lak_attn_full(lak_cache* cache, int32_t layer, const void* q, const void* k_new,

@@ -8,7 +8,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblak.so")
 
 LAK_OK, LAK_EINVAL, LAK_ENOPAGE, LAK_EHIP, LAK_EUNSUPPORTED, LAK_ESTATE = 0, -1, -2, -3, -4, -5
-LAK_BF16, LAK_F32 = 0, 1
+LAK_BF16, LAK_F32, LAK_FP8_E4M3 = 0, 1, 2
 LAK_AGG_MAX, LAK_AGG_SUM = 0, 1
 LAK_SCOPE_GROUP, LAK_SCOPE_ALL = 0, 1
 
@@ -65,6 +65,7 @@ SIGNATURES = {
     "lak_kv_prefill": (_S, [_P, _I32, _P, _P, _I64, _P]),
     "lak_kv_write_rows": (_S, [_P, _I32, _I32, _P, _P, _P, _P]),
     "lak_kv_gather": (_S, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
+    "lak_kv_gather_scales": (_S, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "lak_attn_full": (_S, [_P, _I32, _P, _P, _P, _F, _P, _P, _P, C.c_size_t, _P]),
     "lak_attn_delta_select": (_S, [_P, _I32, _P, _P, _P, _F, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _I32, _P,
                                    _P, C.c_size_t, _P]),

@@ -12,8 +12,10 @@ import torch
 
 from . import _lib as L
 
-_TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
-_LAK_DT = {"bf16": L.LAK_BF16, "f32": L.LAK_F32}
+# activations (q, out, k_new / v_new, prefill rows) per cache dtype; fp8 pools take bfloat16 rows
+_TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.bfloat16}
+_LAK_DT = {"bf16": L.LAK_BF16, "f32": L.LAK_F32, "fp8": L.LAK_FP8_E4M3}
+_POOL_DT = {"bf16": (torch.bfloat16, 2), "f32": (torch.float32, 4), "fp8": (torch.uint8, 1)}
 _AGG = {"max": L.LAK_AGG_MAX, "sum": L.LAK_AGG_SUM}
 _SCOPE = {"group": L.LAK_SCOPE_GROUP, "all": L.LAK_SCOPE_ALL}
 
@@ -52,9 +54,10 @@ class PagedKVCache:
         pool_bytes = lib.lak_pool_bytes(C.byref(desc))
         if pool_bytes <= 0:
             raise L.LakError(L.LAK_EINVAL, "lak_pool_bytes", "invalid description")
-        elems = pool_bytes // (2 if dtype == "bf16" else 4)
-        self.k_pools = [torch.empty(elems, dtype=self.torch_dtype, device=self.device) for _ in range(num_layers)]
-        self.v_pools = [torch.empty(elems, dtype=self.torch_dtype, device=self.device) for _ in range(num_layers)]
+        pdt, esz = _POOL_DT[dtype]
+        elems = pool_bytes // esz
+        self.k_pools = [torch.empty(elems, dtype=pdt, device=self.device) for _ in range(num_layers)]
+        self.v_pools = [torch.empty(elems, dtype=pdt, device=self.device) for _ in range(num_layers)]
         self.page_table = torch.zeros((max_batch, max_pages_per_seq), dtype=torch.int32, device=self.device)
         self.seq_lens = torch.zeros(max_batch, dtype=torch.int32, device=self.device)
         kp = (C.c_void_p * num_layers)(*[t.data_ptr() for t in self.k_pools])
@@ -123,9 +126,19 @@ class PagedKVCache:
                                           _stream()), "lak_kv_write_rows")
 
     def kv_gather(self, layer, b, g, t0, n):
-        k = torch.empty((n, self.d), dtype=self.torch_dtype, device=self.device)
-        v = torch.empty((n, self.d), dtype=self.torch_dtype, device=self.device)
+        """Rows [t0, t0+n) of (b, g) in the pool's element type (uint8 E4M3 codes for fp8)."""
+        pdt = _POOL_DT[self.dtype][0]
+        k = torch.empty((n, self.d), dtype=pdt, device=self.device)
+        v = torch.empty((n, self.d), dtype=pdt, device=self.device)
         L.check(L.lib().lak_kv_gather(self._h, layer, b, g, t0, n, _ptr(k), _ptr(v), _stream()), "lak_kv_gather")
+        return k, v
+
+    def kv_gather_scales(self, layer, b, g, t0, n):
+        """fp8 caches: the float32 scales of rows [t0, t0+n) of (b, g)."""
+        k = torch.empty(n, dtype=torch.float32, device=self.device)
+        v = torch.empty(n, dtype=torch.float32, device=self.device)
+        L.check(L.lib().lak_kv_gather_scales(self._h, layer, b, g, t0, n, _ptr(k), _ptr(v), _stream()),
+                "lak_kv_gather_scales")
         return k, v
 
     # ------------------------------------------------------------ attention

@@ -46,7 +46,14 @@ constexpr int kMinSubtilesPerWg = 8;
 constexpr int kMaxItemsPerSplit = 256;
 constexpr int kScoreTokensPerBlock = 2048;
 
-int esize(int dtype) { return dtype == LAK_BF16 ? 2 : 4; }
+int esize(int dtype) { return dtype == LAK_BF16 ? 2 : (dtype == LAK_FP8_E4M3 ? 1 : 4); }
+
+bool valid_dtype(int dtype) { return dtype == LAK_BF16 || dtype == LAK_F32 || dtype == LAK_FP8_E4M3; }
+
+// Bytes of one pool's element codes; fp8 pools hold one float32 scale per token row after them.
+int64_t code_bytes(const lak_cache_desc& d) {
+  return d.num_pages * d.num_kv_heads * (int64_t)d.page_size * d.head_dim * esize(d.dtype);
+}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -169,6 +176,7 @@ KvGeom geom(const lak_cache* c) {
   g.page = c->d.page_size;
   g.max_pages = c->d.max_pages_per_seq;
   g.esz = esize(c->d.dtype);
+  g.scale_off = code_bytes(c->d);
   return g;
 }
 
@@ -199,6 +207,18 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
 
   DecodeArgs a;
   std::memset(&a, 0, sizeof(a));
+  hipError_t e = hipSuccess;
+  if (d.dtype == LAK_FP8_E4M3) {
+    // fp8 rows are encoded with a per-row scale by the append kernel first (the
+    // decode kernel then reads the token from the pool like any other)
+    if (k_new) {
+      e = launch_append(geom(c), c->kp[layer], c->vp[layer], d.page_table, d.seq_lens, k_new, v_new, c->batch, st);
+      if (e != hipSuccess) return hip_fail(e, "append launch");
+    }
+    k_new = v_new = nullptr;
+    a.k_scale = reinterpret_cast<const float*>(static_cast<const char*>(c->kp[layer]) + code_bytes(d));
+    a.v_scale = reinterpret_cast<const float*>(static_cast<const char*>(c->vp[layer]) + code_bytes(d));
+  }
   a.k_pool = c->kp[layer];
   a.v_pool = c->vp[layer];
   a.page_table = d.page_table;
@@ -227,7 +247,6 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
     a.sum_pairs = (mode == MODE_DELTA && agg == LAK_AGG_SUM) ? 1 : 0;
   }
   a.t_pad = (int64_t)d.max_pages_per_seq * d.page_size;
-  hipError_t e = hipSuccess;
   if (c->trace_before) e = hipEventRecord(c->trace_before, st);
   if (e == hipSuccess) e = launch_decode(d.dtype, mode, d.head_dim, a, splits, c->batch, st);
   if (e == hipSuccess && c->trace_after) e = hipEventRecord(c->trace_after, st);
@@ -290,9 +309,10 @@ extern "C" {
 
 int64_t lak_pool_bytes(const lak_cache_desc* d) {
   if (!d || d->num_pages <= 0 || d->num_kv_heads <= 0 || d->page_size <= 0 || d->head_dim <= 0 ||
-      (d->dtype != LAK_BF16 && d->dtype != LAK_F32))
+      !valid_dtype(d->dtype))
     return -1;
-  return d->num_pages * d->num_kv_heads * (int64_t)d->page_size * d->head_dim * esize(d->dtype);
+  const int64_t scales = d->dtype == LAK_FP8_E4M3 ? d->num_pages * d->num_kv_heads * (int64_t)d->page_size * 4 : 0;
+  return code_bytes(*d) + scales;
 }
 
 lak_status lak_cache_create(const lak_cache_desc* desc, lak_cache** out) {
@@ -303,7 +323,7 @@ lak_status lak_cache_create(const lak_cache_desc* desc, lak_cache** out) {
     return fail(LAK_EINVAL, "all sizes must be positive");
   if (d.num_q_heads % d.num_kv_heads != 0)
     return fail(LAK_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", d.num_q_heads, d.num_kv_heads);
-  if (d.dtype != LAK_BF16 && d.dtype != LAK_F32) return fail(LAK_EINVAL, "bad dtype %d", d.dtype);
+  if (!valid_dtype(d.dtype)) return fail(LAK_EINVAL, "bad dtype %d", d.dtype);
   if (d.num_pages > 0x7FFFFFFF) return fail(LAK_EINVAL, "num_pages exceeds int32 page ids");
   const int G = d.num_q_heads / d.num_kv_heads;
   if (G > 16) return fail(LAK_EUNSUPPORTED, "group size %d > 16", G);
@@ -516,6 +536,22 @@ lak_status lak_kv_gather(lak_cache* c, int32_t layer, int32_t b, int32_t g, int3
     return fail(LAK_EINVAL, "tokens [%d, %lld) outside [0, %d)", t0, (long long)t0 + n, c->lens[b]);
   hipError_t e = launch_gather(geom(c), c->kp[layer], c->vp[layer], c->d.page_table, b, g, t0, n, k_out, v_out,
                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return ok();
+}
+
+lak_status lak_kv_gather_scales(lak_cache* c, int32_t layer, int32_t b, int32_t g, int32_t t0, int32_t n,
+                                float* k_out, float* v_out, void* stream) {
+  lak_status s = check_cache(c, true);
+  if (s != LAK_OK) return s;
+  if ((s = check_layer(c, layer)) != LAK_OK) return s;
+  if (c->d.dtype != LAK_FP8_E4M3) return fail(LAK_EINVAL, "only fp8 pools have scales");
+  if (b < 0 || b >= c->batch) return fail(LAK_EINVAL, "sequence %d not active", b);
+  if (g < 0 || g >= c->d.num_kv_heads) return fail(LAK_EINVAL, "kv head %d out of range", g);
+  if (t0 < 0 || n < 0 || (int64_t)t0 + n > c->lens[b])
+    return fail(LAK_EINVAL, "tokens [%d, %lld) outside [0, %d)", t0, (long long)t0 + n, c->lens[b]);
+  hipError_t e = launch_gather_scales(geom(c), c->kp[layer], c->vp[layer], c->d.page_table, b, g, t0, n, k_out,
+                                      v_out, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gather launch");
   return ok();
 }

@@ -39,11 +39,12 @@ template <int D>
 struct Frag<2, D> {
   static constexpr int NL = D / 32;  // 16-byte loads per lane per operand
   static constexpr int NO = D / 16;  // 16-row output tiles of O^T
+  static constexpr int NQ = D / 32;  // q operands
   u32x4 k[NL], v[NL];
   typedef bf16x8 QF;
 
   template <bool STREAM>
-  __device__ inline void load(const uint16_t* kb, const uint16_t* vb, int lane) {
+  __device__ inline void load(const uint16_t* kb, const uint16_t* vb, const float*, const float*, int lane) {
     const u32x4* kp = reinterpret_cast<const u32x4*>(kb);
     const u32x4* vp = reinterpret_cast<const u32x4*>(vb);
 #pragma unroll
@@ -120,11 +121,12 @@ template <int D>
 struct Frag<4, D> {
   static constexpr int NL = D / 16;
   static constexpr int NO = D / 16;
+  static constexpr int NQ = D / 16;
   u32x4 k[NL], v[NL];
   typedef f32x4 QF;
 
   template <bool STREAM>
-  __device__ inline void load(const uint32_t* kb, const uint32_t* vb, int lane) {
+  __device__ inline void load(const uint32_t* kb, const uint32_t* vb, const float*, const float*, int lane) {
     const u32x4* kp = reinterpret_cast<const u32x4*>(kb);
     const u32x4* vp = reinterpret_cast<const u32x4*>(vb);
 #pragma unroll
@@ -178,8 +180,96 @@ struct Frag<4, D> {
   }
 };
 
+// fp8 (OCP E4M3 codes, one float32 scale per token): the codes are widened to
+// bfloat16 in registers (exact: every E4M3 value is a bfloat16 value) and go
+// through the same bf16 MFMAs; the key scale of a token multiplies its logit and
+// the value scale its probability, so no element is rescaled.
+template <int D>
+struct Frag<1, D> {
+  static constexpr int NL = D / 64;  // 16-byte loads per lane per operand
+  static constexpr int NO = D / 16;
+  static constexpr int NQ = D / 32;
+  u32x4 k[NL], v[NL];
+  u32x4 ks, vs;  // float bits of the key / value scales of tokens 4(l/16) .. +4
+  typedef bf16x8 QF;
+
+  template <bool STREAM>
+  __device__ inline void load(const uint8_t* kb, const uint8_t* vb, const float* ksb, const float* vsb,
+                              int lane) {
+    const u32x4* kp = reinterpret_cast<const u32x4*>(kb);
+    const u32x4* vp = reinterpret_cast<const u32x4*>(vb);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) k[i] = load16<STREAM>(kp + i * 64 + lane);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) v[i] = load16<STREAM>(vp + i * 64 + lane);
+    ks = load16<STREAM>(reinterpret_cast<const u32x4*>(ksb) + (lane >> 4));
+    vs = load16<STREAM>(reinterpret_cast<const u32x4*>(vsb) + (lane >> 4));
+  }
+  // Lane l of load i holds token l%16, head-dim elements 16(4i + l/16) .. +16; the
+  // first 8 feed MFMA 2i, the other 8 MFMA 2i+1, so q operand m of lane l holds
+  // head l%16, elements 64(m/2) + 16(l/16) + 8(m%2) .. +8.
+  __device__ static inline void load_q(QF* qf, const uint16_t* qrow, bool valid, int j) {
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (valid) w = *reinterpret_cast<const u32x4*>(qrow + 64 * (m >> 1) + 16 * j + 8 * (m & 1));
+      qf[m] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  // 2 E4M3 codes (bytes 0-1, or 2-3 for HI) of a word -> 2 bfloat16 in one word
+  template <bool HI>
+  __device__ static inline uint32_t widen2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  }
+  __device__ inline f32x4 qk(const QF* qf) const {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 a = {widen2<false>(k[i][2 * h]), widen2<true>(k[i][2 * h]), widen2<false>(k[i][2 * h + 1]),
+                         widen2<true>(k[i][2 * h + 1])};
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qf[2 * i + h], s, 0, 0, 0);
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] *= __uint_as_float(ks[r]);
+    return s;
+  }
+  // zero the codes of tokens >= nvalid (token of byte e of a word is 4(l/16) + e)
+  __device__ inline void mask_v(int nvalid, int j) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * j + e >= nvalid) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) v[i][x] &= ~(0xFFu << (8 * e));
+      }
+  }
+  // Word x of load i holds the codes of tokens 4(l/16) .. +4 at head-dim element
+  // 16(4i + x) + l%16: the A operand of output tile 4i + x.
+  __device__ inline void pv(f32x4* o, const float* p) const {
+    float w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w[r] = (p[r] == 0.f) ? 0.f : p[r] * __uint_as_float(vs[r]);
+    const uint32_t w0 = (uint32_t)f32_to_bf16_rne(w[0]) | ((uint32_t)f32_to_bf16_rne(w[1]) << 16);
+    const uint32_t w1 = (uint32_t)f32_to_bf16_rne(w[2]) | ((uint32_t)f32_to_bf16_rne(w[3]) << 16);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const i16x4 pf = __builtin_bit_cast(i16x4, (u32x2){w0, w1});
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const i16x4 va = __builtin_bit_cast(i16x4, (u32x2){widen2<false>(v[i][x]), widen2<true>(v[i][x])});
+        o[4 * i + x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pf, o[4 * i + x], 0, 0, 0);
+      }
+  }
+};
+
 template <int ESZ>
 struct ElemT;
+template <>
+struct ElemT<1> { typedef uint8_t T; };
 template <>
 struct ElemT<2> { typedef uint16_t T; };
 template <>
@@ -189,6 +279,7 @@ struct ElemT<4> { typedef uint32_t T; };
 template <int ESZ, int D, int MODE, int U>
 __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_kernel(DecodeArgs a) {
   typedef typename ElemT<ESZ>::T E;
+  typedef typename ElemT<ESZ == 1 ? 2 : ESZ>::T QE;  // q rows: bfloat16 for fp8 pools
   typedef Frag<ESZ, D> F;
   extern __shared__ __align__(16) float lds[];
 
@@ -211,7 +302,7 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
   // takes the token from k_new / v_new directly (see `patch` below).
   const E* krow_new = nullptr;
   const E* vrow_new = nullptr;
-  if (a.k_new != nullptr && T > 0) {
+  if (ESZ != 1 && a.k_new != nullptr && T > 0) {
     krow_new = reinterpret_cast<const E*>(a.k_new) + ((int64_t)b * a.hkv + g) * D;
     vrow_new = reinterpret_cast<const E*>(a.v_new) + ((int64_t)b * a.hkv + g) * D;
     if (s == 0) {
@@ -240,8 +331,8 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
   const int n = lane & 15, j = lane >> 4;
   const bool head_ok = n < G;
 
-  typename F::QF qf[F::NL];
-  F::load_q(qf, reinterpret_cast<const E*>(a.q) + ((int64_t)b * a.hq + g * G + (head_ok ? n : 0)) * D,
+  typename F::QF qf[F::NQ];
+  F::load_q(qf, reinterpret_cast<const QE*>(a.q) + ((int64_t)b * a.hq + g * G + (head_ok ? n : 0)) * D,
             head_ok, j);
 
   const E* kpool = reinterpret_cast<const E*>(a.k_pool);
@@ -283,8 +374,9 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
     const int t0 = lp * P + sub * kSub;
     const bool valid = lp >= 0 && t0 < T;
     const int64_t phys = __builtin_amdgcn_readlane(pid_vec, k);
-    const int64_t base = valid ? ((phys * a.hkv + g) * P + sub * kSub) * (int64_t)D : 0;
-    f.template load<MODE != MODE_SPARSE>(kpool + base, vpool + base, lane);
+    const int64_t row0 = valid ? (phys * a.hkv + g) * P + sub * kSub : 0;  // first token row
+    f.template load<MODE != MODE_SPARSE>(kpool + row0 * D, vpool + row0 * D, a.k_scale + row0,
+                                         a.v_scale + row0, lane);
     return Sub{valid, t0};
   };
 
@@ -295,7 +387,9 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
   for (int x = 0; x < F::NO; ++x) o[x] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   auto process = [&](F& f, int ct, int x) {
-    if (krow_new != nullptr && T - 1 < ct + kSub) f.patch(krow_new, vrow_new, (T - 1) - ct, lane);
+    if constexpr (ESZ != 1) {
+      if (krow_new != nullptr && T - 1 < ct + kSub) f.patch(krow_new, vrow_new, (T - 1) - ct, lane);
+    }
     const f32x4 sacc = f.qk(qf);
     const int tb = ct + 4 * j;
     float s2[4];
@@ -538,6 +632,9 @@ hipError_t launch_decode(int dtype, int mode, int D, const DecodeArgs& a, int sp
   if (dtype == 0) {
     if (D == 128) return launch_decode_t<2, 128>(mode, a, splits, batch, st);
     if (D == 64) return launch_decode_t<2, 64>(mode, a, splits, batch, st);
+  } else if (dtype == 2) {
+    if (D == 128) return launch_decode_t<1, 128>(mode, a, splits, batch, st);
+    if (D == 64) return launch_decode_t<1, 64>(mode, a, splits, batch, st);
   } else {
     if (D == 128) return launch_decode_t<4, 128>(mode, a, splits, batch, st);
     if (D == 64) return launch_decode_t<4, 64>(mode, a, splits, batch, st);
@@ -548,6 +645,7 @@ hipError_t launch_decode(int dtype, int mode, int D, const DecodeArgs& a, int sp
 hipError_t launch_combine(int dtype, int D, const CombineArgs& a, int batch, hipStream_t st) {
   if (batch == 0) return hipSuccess;
   dim3 grid(a.hq, batch);
+  if (dtype == 2) dtype = 0;  // fp8 pools: bfloat16 outputs
   if (dtype == 0 && D == 128) hipLaunchKernelGGL((combine_kernel<2, 128>), grid, dim3(64), 0, st, a);
   else if (dtype == 0 && D == 64) hipLaunchKernelGGL((combine_kernel<2, 64>), grid, dim3(64), 0, st, a);
   else if (dtype == 1 && D == 128) hipLaunchKernelGGL((combine_kernel<4, 128>), grid, dim3(64), 0, st, a);

@@ -40,6 +40,9 @@ __host__ __device__ inline int v_off(int tt, int d) {
   return (((d / (16 * H)) * 4 + tt / 4) * 16 + d % 16) * (4 * H) + ((d / 16) % H) * 4 + tt % 4;
 }
 
+// fp8 pools (esz 1) use the same formulas with W = 16 codes per lane and H = 4;
+// their per-token float32 scales follow all pages' codes as [page][Hkv][P].
+
 // Element offset of (physical page, kv head, token-in-page) sub-tile start.
 __device__ inline int64_t subtile_base(int64_t phys, int g, int t_in_page, int hkv, int P, int D) {
   return ((phys * hkv + g) * P + (t_in_page / kSub) * kSub) * (int64_t)D;
@@ -58,6 +61,31 @@ __device__ inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(b >> 16);
 }
 __device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// ---------------------------------------------------------------------------
+// fp8 rows: OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+// largest magnitude 448) with one float32 scale per row of D values:
+// scale = max|x| / 448, code = round-to-nearest-even(x / scale) after clamping to
+// +-448; a row whose scale is 0 gets codes 0.
+// ---------------------------------------------------------------------------
+constexpr float kE4m3Max = 448.0f;
+
+__device__ inline float e4m3_row_scale(float amax) { return amax / kE4m3Max; }
+
+// Codes of x0 / scale and x1 / scale in the low two bytes (x0 in byte 0).
+__device__ inline uint32_t e4m3_encode2(float x0, float x1, float scale) {
+  if (!(scale > 0.f)) return 0u;
+  const float a = fminf(fmaxf(x0 / scale, -kE4m3Max), kE4m3Max);
+  const float b = fminf(fmaxf(x1 / scale, -kE4m3Max), kE4m3Max);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// Wave-wide maximum (64 lanes).
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
 
 // Inclusive prefix sum over a wave (64 lanes).
 __device__ inline int wave_incl_scan(int v, int lane) {

@@ -16,7 +16,9 @@ struct DecodeArgs {
   const int32_t* seq_lens;     // [max_batch]
   const void* q;               // [B][Hq][D]
   const void* k_new;           // optional [B][Hkv][D]: token appended at T-1 by this call
-  const void* v_new;
+  const void* v_new;           // (never set for fp8 pools: their append is a separate launch)
+  const float* k_scale;        // fp8 pools: per-token scales [page][Hkv][P] after the codes
+  const float* v_scale;
   float sm_scale;
   int hq, hkv, page, max_pages;
   int pps;                     // items (pages or selection entries) per split
@@ -83,7 +85,8 @@ struct StepUpdate {
 };
 
 struct KvGeom {
-  int hkv, d, page, max_pages, esz;
+  int hkv, d, page, max_pages, esz;  // esz 1: fp8 codes (bfloat16 rows in and out of the library)
+  int64_t scale_off;                 // fp8: byte offset of the [page][Hkv][P] float32 scales in a pool
 };
 
 // Tuning knobs, read once from the environment (defaults are the tuned values):
@@ -117,5 +120,7 @@ hipError_t launch_write_rows(const KvGeom& g, void* kp, void* vp, const int32_t*
                              const void* vr, int batch, hipStream_t st);
 hipError_t launch_gather(const KvGeom& g, const void* kp, const void* vp, const int32_t* pt,
                          int b, int gh, int t0, int n, void* ko, void* vo, hipStream_t st);
+hipError_t launch_gather_scales(const KvGeom& g, const void* kp, const void* vp, const int32_t* pt,
+                                int b, int gh, int t0, int n, float* ko, float* vo, hipStream_t st);
 
 }  // namespace lak

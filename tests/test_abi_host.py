@@ -57,6 +57,12 @@ def test_pool_bytes():
     assert L.lib().lak_pool_bytes(C.byref(d)) == 10 * 4 * 16 * 128 * 2
     d = _desc(num_pages=3, hkv=2, page=32, d=64, dtype=L.LAK_F32)
     assert L.lib().lak_pool_bytes(C.byref(d)) == 3 * 2 * 32 * 64 * 4
+    # fp8: one byte per code plus a float32 scale per (page, kv head, token) row
+    d = _desc(num_pages=5, hkv=4, page=16, d=128, dtype=L.LAK_FP8_E4M3)
+    assert L.lib().lak_pool_bytes(C.byref(d)) == 5 * 4 * 16 * 128 + 5 * 4 * 16 * 4
+    st, h = _create(dtype=L.LAK_FP8_E4M3)
+    assert st == L.LAK_OK
+    L.lib().lak_cache_destroy(h)
 
 
 @pytest.mark.parametrize("kw,code", [
