@@ -38,10 +38,11 @@ if ROOT not in sys.path:
 METRIC = "decode attention tokens/s per stack + achieved HBM GB/s (full vs sparse layers)"
 PEAK_HBM_GBPS = 8000.0
 KERNEL_NAMES = {
-    "full": "lak::decode_kernel<2, 128, MODE_FULL>",
-    "delta": "lak::decode_kernel<2, 128, MODE_DELTA>",
-    "sparse": "lak::decode_kernel<2, 128, MODE_SPARSE>",
+    "full": "lak::decode_kernel<{esz}, 128, MODE_FULL>",
+    "delta": "lak::decode_kernel<{esz}, 128, MODE_DELTA>",
+    "sparse": "lak::decode_kernel<{esz}, 128, MODE_SPARSE>",
 }
+KV_ESZ = {"bf16": 2, "f32": 4, "fp8": 1}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -85,7 +86,7 @@ class Tracer:
 class StackBench:
     """Device set-up and the step loop of one stack workload (inputs resident in HBM)."""
 
-    def __init__(self, wl, warmup, steps, agg="max", scope="group"):
+    def __init__(self, wl, warmup, steps, agg="max", scope="group", kv_dtype=None):
         import torch
         from layer_aware_kv_amd import PagedKVCache, layer_tiers
         from workload import Recipe
@@ -103,7 +104,8 @@ class StackBench:
         B, L, P = wl.batch, wl.num_layers, wl.page
         max_pages = math.ceil((max(self.lens0) + self.S) / P) + 1
         num_pages = sum(math.ceil((t + self.S) / P) for t in self.lens0)
-        self.cache = PagedKVCache(L, B, wl.hq, wl.hkv, wl.d, P, max_pages, num_pages, wl.dtype)
+        self.kv_dtype = kv_dtype or wl.dtype
+        self.cache = PagedKVCache(L, B, wl.hq, wl.hkv, wl.d, P, max_pages, num_pages, self.kv_dtype)
         self.cache.seq_reset(self.lens0, reserve_tokens=self.S)
         self.dirty = False
         self.prefill_all()
@@ -184,6 +186,8 @@ def main():
                     help="heads aggregated per selection: each KV group, or all query heads")
     ap.add_argument("--delta-layers", default=None,
                     help="comma-separated delta-layer list replacing the workload's (sweeps)")
+    ap.add_argument("--kv-dtype", choices=["bf16", "fp8"], default=None,
+                    help="KV pool element type (default: the workload's; fp8 = E4M3 codes + per-row scales)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (for HBM counter scaling)")
     args = ap.parse_args()
@@ -216,15 +220,20 @@ def main():
     K = wl.steps if args.steps is None else args.steps
     B, L, HQ, HKV, D, P = wl.batch, wl.num_layers, wl.hq, wl.hkv, wl.d, wl.page
     e = 2 if wl.dtype == "bf16" else 4
+    kv_dtype = args.kv_dtype or wl.dtype
+    if kv_dtype == "fp8" and wl.dtype != "bf16":
+        sys.exit("fp8 pools take bfloat16 rows: use a bf16 workload")
+    kv_row = acc.kv_row_bytes(D, kv_dtype)
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name} ({props.multi_processor_count} CUs), workload {wl.name}, W={W} K={K}")
 
     t_setup = time.perf_counter()
-    sb = StackBench(wl, W, K, agg=args.agg, scope=args.scope)
+    sb = StackBench(wl, W, K, agg=args.agg, scope=args.scope, kv_dtype=kv_dtype)
     lens0, tiers, rec = sb.lens0, sb.tiers, sb.rec
-    log(f"set-up {time.perf_counter() - t_setup:.1f} s: {2 * L * sb.cache.k_pools[0].numel() * e / 1e9:.1f} GB "
-        f"of KV pools; drift events at steps {sorted(sb.drift)}")
+    pool_gb = 2 * L * sb.cache.k_pools[0].numel() * sb.cache.k_pools[0].element_size() / 1e9
+    log(f"set-up {time.perf_counter() - t_setup:.1f} s: {pool_gb:.1f} GB of {kv_dtype} KV pools; "
+        f"drift events at steps {sorted(sb.drift)}")
 
     # decode-kernel bytes of one launch at step s
     def kernel_bytes(tier, s):
@@ -232,11 +241,11 @@ def main():
         q_bytes = B * HQ * D * e
         if tier == "sparse":
             toks = sum(acc.selected_tokens(t, P, wl.k_top, wl.recency) for t in lens)
-            return toks * HKV * D * 2 * e + q_bytes + B * HKV * (wl.k_top + wl.recency) * 4
-        return sum(lens) * HKV * D * 2 * e + q_bytes
+            return toks * HKV * kv_row * 2 + q_bytes + B * HKV * (wl.k_top + wl.recency) * 4
+        return sum(lens) * HKV * kv_row * 2 + q_bytes
 
     mid = [t + W + K // 2 + 1 for t in lens0]
-    step_bytes = acc.stack_bytes(mid, tiers, HQ, HKV, D, e, P, wl.k_top, wl.recency)
+    step_bytes = acc.stack_bytes(mid, tiers, HQ, HKV, D, e, P, wl.k_top, wl.recency, kv_row)
     present = sorted(set(tiers))
     dom = max(present, key=lambda t: step_bytes[t])
 
@@ -286,7 +295,8 @@ def main():
             with open(TRAFFIC_FILE) as f:
                 tj = json.load(f)
             ent = tj.get("kernels", {}).get(dom)
-            if tj.get("source_hash") == kernel_source_hash() and tj.get("workload") == wl.name and ent:
+            if (tj.get("source_hash") == kernel_source_hash() and tj.get("workload") == wl.name and ent
+                    and tj.get("kv_dtype", wl.dtype) == kv_dtype):
                 traffic = ent["hbm_bytes_per_launch"]
         except (OSError, ValueError, KeyError):
             traffic = None
@@ -309,11 +319,12 @@ def main():
             "layers": L, "batch": B, "context": wl.context, "q_heads": HQ, "kv_heads": HKV, "head_dim": D,
             "page": P, "top_k_pages": wl.k_top, "recency_pages": wl.recency,
             "full_layers": list(wl.full_layers), "delta_layers": list(wl.delta_layers),
-            "ragged_min": wl.ragged_min, "agg": args.agg, "scope": args.scope, "parallelism": "single GPU",
+            "ragged_min": wl.ragged_min, "agg": args.agg, "scope": args.scope, "kv_dtype": kv_dtype,
+            "parallelism": "single GPU",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": KERNEL_NAMES[dom],
+            "kernel": KERNEL_NAMES[dom].format(esz=KV_ESZ[kv_dtype]),
             "achieved": round(domA["achieved_GBps"], 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
@@ -343,7 +354,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, rec, tiers, W, args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(wl, rec, tiers, W, args.cpu_rows, kv_dtype)
     print(json.dumps(result), flush=True)
 
 
@@ -373,9 +384,11 @@ def fidelity_pass(sb, torch):
     return fidelity.summarize(recalls, errors)
 
 
-def cpu_baseline(wl, rec, tiers, step, rows, repeats=3):
+def cpu_baseline(wl, rec, tiers, step, rows, kv_dtype, repeats=3):
     """The CPU oracle, as it stands, on a bounded sample: one decode step of ``rows``
-    batch rows through one layer of each tier, extrapolated to the stack's tier counts."""
+    batch rows through one layer of each tier, extrapolated to the stack's tier counts.
+    fp8 pools: the rows are encoded and decoded by the oracle before timing (the
+    cache holds them encoded), and attention runs on the decoded values."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -394,6 +407,8 @@ def cpu_baseline(wl, rec, tiers, step, rows, repeats=3):
             for t, layer in first.items():
                 src = layer if t != "sparse" else first.get("delta", layer)
                 K, V = rec.layer_kv(layer, b, T, epoch)
+                if kv_dtype == "fp8":
+                    K, V = oracle.quant.quantize_dequantize(K), oracle.quant.quantize_dequantize(V)
                 data[t] = (rec.q(layer, step, b), K, V, src)
             for _ in range(repeats):
                 sel = None

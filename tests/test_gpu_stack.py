@@ -22,13 +22,14 @@ SAMPLES = {
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("index", [2, 3, 4])
-def test_stack_full_size_sampled(index):
+@pytest.mark.parametrize("index,kv", [(2, None), (3, None), (4, None), (3, "fp8")])
+def test_stack_full_size_sampled(index, kv):
     import bench
+    from oracle.quant import quantize_dequantize
     wl = CONFIGS[index]
     spec = SAMPLES[index]
-    print(f"stack parity: {wl.name}", flush=True)
-    sb = bench.StackBench(wl, spec["warmup"], spec["steps"])
+    print(f"stack parity: {wl.name} kv {kv or wl.dtype}", flush=True)
+    sb = bench.StackBench(wl, spec["warmup"], spec["steps"], kv_dtype=kv)
     rec, tiers, lens0 = sb.rec, sb.tiers, sb.lens0
     rows = spec["rows"] or [int(np.argmin(lens0)), int(np.argmax(lens0))]
     deltas = [l for l, t in enumerate(tiers) if t == "delta"]
@@ -61,6 +62,8 @@ def test_stack_full_size_sampled(index):
             for layer in spec["layers"]:
                 tier = tiers[layer]
                 K, V = rec.layer_kv(layer, b, T, epoch)
+                if kv == "fp8":
+                    K, V = quantize_dequantize(K), quantize_dequantize(V)
                 q = rec.q(layer, s, b)
                 got, got_lse = cap["out"][layer][i], cap["lse"][layer][i]
                 what = f"{wl.name} step {s} row {b} layer {layer} ({tier})"
