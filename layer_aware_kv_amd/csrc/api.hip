@@ -39,7 +39,7 @@ lak_status hip_fail(hipError_t e, const char* where) {
 // LAK_TUNE_TARGET_WGS overrides) and the fewest 16-token sub-tiles one workgroup
 // is given.
 constexpr int kTargetWgs = 1024;
-constexpr int kTargetWgsDelta = 4096;  // smaller delta splits spread the logits writes
+constexpr int kTargetWgsDelta = 1536;  // smaller delta splits spread the scratch writes
 constexpr int kMinSubtilesPerWg = 8;
 // Each of the 4 waves of a decode workgroup keeps the page ids of its items in one
 // register per lane, so a split holds at most 4 * 64 items.
@@ -118,7 +118,7 @@ struct lak_cache {
 namespace {
 
 struct WsLayout {
-  size_t o_part, ml_part, lse, logits, scores, total;
+  size_t o_part, ml_part, lse, logits, rel_max, scores, total;
 };
 
 WsLayout ws_layout(const lak_cache* c) {
@@ -134,11 +134,16 @@ WsLayout ws_layout(const lak_cache* c) {
   off = align256(off + part * 2 * sizeof(float));
   w.lse = off;
   off = align256(off + rows_h * sizeof(float));
-  w.logits = off;  // [B][Hkv][sub-tiles][Gp][16], Gp = G rounded up to even
+  // delta scratch: fp16 relative weights [B][Hkv][sub-tiles][Gp][16] (MAX) or the
+  // (max, sum) pairs [B][Hkv][sub-tiles][Gp][2] float (SUM), then the sub-tile maxima
+  // [B][Hkv][sub-tiles][Gp] float (MAX); Gp = G rounded up to even
+  w.logits = off;
   const int G = d.num_q_heads / d.num_kv_heads;
   const size_t gp = (size_t)(G + (G & 1));
-  off = align256(off + (size_t)d.max_batch * d.num_kv_heads * gp * (size_t)d.max_pages_per_seq * d.page_size *
-                           sizeof(float));
+  const size_t blocks = (size_t)d.max_batch * d.num_kv_heads * gp * ((size_t)d.max_pages_per_seq * d.page_size / 16);
+  off = align256(off + blocks * 16 * 2);
+  w.rel_max = off;
+  off = align256(off + blocks * sizeof(float));
   w.scores = off;
   off = align256(off + (size_t)d.max_batch * d.num_kv_heads * d.max_pages_per_seq * sizeof(float));
   w.total = off;
@@ -240,9 +245,11 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
   a.o_part = reinterpret_cast<float*>(wsb + w.o_part);
   a.ml_part = reinterpret_cast<float*>(wsb + w.ml_part);
   a.logits = reinterpret_cast<float*>(wsb + w.logits);
+  a.rel_w = reinterpret_cast<uint16_t*>(wsb + w.logits);
+  a.rel_max = reinterpret_cast<float*>(wsb + w.rel_max);
   {
     const int G = d.num_q_heads / d.num_kv_heads;
-    const size_t staged = (size_t)pps * (d.page_size / 16) * (G + (G & 1)) * 16 * sizeof(float);
+    const size_t staged = delta_stage_bytes(pps, d.page_size, G);
     a.lds_logits = (mode == MODE_DELTA && tune_delta_lds() && staged <= 64 * 1024) ? 1 : 0;
     a.sum_pairs = (mode == MODE_DELTA && agg == LAK_AGG_SUM) ? 1 : 0;
   }
@@ -590,6 +597,8 @@ lak_status lak_attn_delta_select(lak_cache* c, int32_t layer, const void* q, con
   float* scores = page_scores ? page_scores : reinterpret_cast<float*>(wsb + w.scores);
   PageScoreArgs pa;
   pa.logits = reinterpret_cast<const float*>(wsb + w.logits);
+  pa.rel_w = reinterpret_cast<const uint16_t*>(wsb + w.logits);
+  pa.rel_max = reinterpret_cast<const float*>(wsb + w.rel_max);
   pa.lse = reinterpret_cast<const float*>(wsb + w.lse);
   pa.seq_lens = c->d.seq_lens;
   pa.scores = scores;

@@ -1,9 +1,11 @@
 // Split-K decode attention over the paged KV cache, for the three layer tiers of
 // DELTA ("Methodology in Plain English", DELTA AI summary page):
 //   MODE_FULL   full attention (layers 0-1),
-//   MODE_DELTA  full attention that also writes the scaled logits of every valid
-//               token (the delta-layer scores are taken from the decode kernel's
-//               own logits, as the pages' implementation does),
+//   MODE_DELTA  full attention that also writes what the page scores need of every
+//               valid token's logit (the delta-layer scores are taken from the decode
+//               kernel's own logits, as the pages' implementation does): per head and
+//               16-token sub-tile the max logit and fp16 weights relative to it (MAX
+//               aggregation), or the (max, sum of exponentials) pair (SUM),
 //   MODE_SPARSE attention over the tokens of the selected pages only.
 // One workgroup = one (sequence b, KV head g, split s); a row's pages are dealt to
 // its splits round-robin and a split's 4 waves take its pages in turn.  Per sub-tile: S^T = K Q^T with the G query heads
@@ -380,6 +382,9 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
     return Sub{valid, t0};
   };
 
+  // delta tier, LDS staging: fp16 blocks of the split's sub-tiles, then their maxima
+  const int lds_r_off = (a.pps * spp * Gp * kSub) / 2;  // in floats (2 fp16 per float)
+
   float m2 = -INFINITY;  // running max, log2 units
   float l = 0.f;         // this lane's share of the running sum
   f32x4 o[F::NO];
@@ -401,36 +406,6 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
     }
     mx = fmaxf(mx, shfl_xor_f(mx, 16));
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    if (MODE == MODE_DELTA && a.sum_pairs) {
-      // (r, e) of this head over the sub-tile: r = max logit (log2 units), e = sum of
-      // 2^(logit - r); the page score later is sum_h e * exp(r ln 2 - lse_h)
-      float e = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) e += exp2f(s2[r] - mx);
-      e += shfl_xor_f(e, 16);
-      e += shfl_xor_f(e, 32);
-      if (head_ok && j == 0) {
-        const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + ct / kSub;
-        typedef float f32x2 __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<f32x2*>(a.logits + (blk * Gp + n) * 2) = (f32x2){mx, e};
-      }
-    } else if (MODE == MODE_DELTA && n < Gp) {
-      // Logits block of (b, g, sub-tile): [Gp heads][16 tokens], Gp = G rounded up to
-      // even, so one store instruction writes whole 128-byte lines (the padding head,
-      // if any, is written too).  Plain stores: the block stays cache-resident for the
-      // page-score kernel.
-      f32x4 w;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) w[r] = (head_ok && tb + r < T) ? sacc[r] * a.sm_scale : -INFINITY;
-      if (a.lds_logits) {
-        // staged in LDS at the sub-tile's index within the workgroup; flushed at the end
-        const int li = (wave + kWaves * (x / spp)) * spp + (x % spp);
-        *reinterpret_cast<f32x4*>(lds + (li * Gp + n) * kSub + 4 * j) = w;
-      } else {
-        const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + ct / kSub;
-        *reinterpret_cast<f32x4*>(a.logits + (blk * Gp + n) * kSub + 4 * j) = w;
-      }
-    }
     const float m_new = fmaxf(m2, mx);
     const float alpha = exp2f(m2 - m_new);
     float p[4];
@@ -439,6 +414,56 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
     for (int r = 0; r < 4; ++r) {
       p[r] = exp2f(s2[r] - m_new);
       ps += p[r];
+    }
+    // delta tier: weights relative to this sub-tile's max, 2^(logit - mx) = p * 2^(m_new - mx);
+    // taken from p unless the running max is so far above mx (> 2^64) that p could lose
+    // precision, then computed directly
+    const float to_rel = exp2f(m_new - mx);
+    const bool rel_from_p = (m_new - mx) <= 64.f;
+    if (MODE == MODE_DELTA && a.sum_pairs) {
+      // (r, e) of this head over the sub-tile: r = max logit (log2 units), e = sum of
+      // 2^(logit - r); the page score later is sum_h e * exp(r ln 2 - lse_h)
+      float e = 0.f;
+      if (rel_from_p) {
+        e = ps * to_rel;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e += exp2f(s2[r] - mx);
+      }
+      e += shfl_xor_f(e, 16);
+      e += shfl_xor_f(e, 32);
+      if (head_ok && j == 0) {
+        const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + ct / kSub;
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<f32x2*>(a.logits + (blk * Gp + n) * 2) = (f32x2){mx, e};
+      }
+    } else if (MODE == MODE_DELTA && n < Gp) {
+      // MAX aggregation: this head's max logit r over the sub-tile (log2 units, exact)
+      // and each token's weight relative to it, u = 2^(logit - r) in (0, 1], rounded to
+      // fp16; the page score later is sum_t max_h u * 2^(r - lse_h), so its relative
+      // error is at most 2^-11.  Blocks are [Gp heads][16 tokens] (Gp = G rounded up to
+      // even, so one block is whole 64-byte lines); the padding head writes zeros.
+      uint32_t hw[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const float u0 = !head_ok ? 0.f : (rel_from_p ? p[2 * r] * to_rel : exp2f(s2[2 * r] - mx));
+        const float u1 = !head_ok ? 0.f : (rel_from_p ? p[2 * r + 1] * to_rel : exp2f(s2[2 * r + 1] - mx));
+        hw[r] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)u0) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)u1) << 16);
+      }
+      const float rmax = head_ok ? mx : 0.f;
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      if (a.lds_logits) {
+        // staged in LDS at the sub-tile's index within the workgroup; flushed at the end
+        const int li = (wave + kWaves * (x / spp)) * spp + (x % spp);
+        uint16_t* lu = reinterpret_cast<uint16_t*>(lds);
+        *reinterpret_cast<u32x2*>(lu + (li * Gp + n) * kSub + 4 * j) = (u32x2){hw[0], hw[1]};
+        if (j == 0) lds[lds_r_off + li * Gp + n] = rmax;
+      } else {
+        const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + ct / kSub;
+        *reinterpret_cast<u32x2*>(a.rel_w + (blk * Gp + n) * kSub + 4 * j) = (u32x2){hw[0], hw[1]};
+        if (j == 0) a.rel_max[blk * Gp + n] = rmax;
+      }
     }
     l = l * alpha + ps;
     m2 = m_new;
@@ -465,19 +490,30 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
   }
 
   if (MODE == MODE_DELTA && a.lds_logits && !a.sum_pairs) {
-    // write the workgroup's logits blocks in one burst (whole 16-byte units per thread)
+    // write the workgroup's blocks in one burst: 16-byte units of fp16 weights (two per
+    // head row), then the maxima
     __syncthreads();
-    const int n_units = n_split * spp * Gp * 4;
+    const int n_sub = n_split * spp;
+    const int n_units = n_sub * Gp * 2;
     for (int idx = threadIdx.x; idx < n_units; idx += blockDim.x) {
-      const int q4 = idx & 3;
-      const int hn = (idx >> 2) % Gp;
-      const int li = (idx >> 2) / Gp;
+      const int half = idx & 1;
+      const int hn = (idx >> 1) % Gp;
+      const int li = (idx >> 1) / Gp;
       const int member = li / spp, sub = li - member * spp;
       const int t0 = (s + S_row * member) * P + sub * kSub;
       if (t0 < T) {
         const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + t0 / kSub;
-        *reinterpret_cast<f32x4*>(a.logits + (blk * Gp + hn) * kSub + 4 * q4) =
-            *reinterpret_cast<const f32x4*>(lds + (li * Gp + hn) * kSub + 4 * q4);
+        *reinterpret_cast<u32x4*>(a.rel_w + (blk * Gp + hn) * kSub + 8 * half) =
+            *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(lds) + (li * Gp + hn) * kSub + 8 * half);
+      }
+    }
+    for (int idx = threadIdx.x; idx < n_sub * Gp; idx += blockDim.x) {
+      const int hn = idx % Gp, li = idx / Gp;
+      const int member = li / spp, sub = li - member * spp;
+      const int t0 = (s + S_row * member) * P + sub * kSub;
+      if (t0 < T) {
+        const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + t0 / kSub;
+        a.rel_max[blk * Gp + hn] = lds[lds_r_off + idx];
       }
     }
     __syncthreads();  // the merge below reuses this LDS
@@ -614,7 +650,7 @@ static hipError_t launch_decode_t(int mode, const DecodeArgs& a, int splits, int
   const int G = a.hq / a.hkv;
   size_t lds = (size_t)(kWaves * G * D + 2 * kWaves * 16) * sizeof(float);
   if (mode == MODE_DELTA && a.lds_logits && !a.sum_pairs)
-    lds = std::max(lds, (size_t)a.pps * (a.page / kSub) * (G + (G & 1)) * kSub * sizeof(float));
+    lds = std::max(lds, delta_stage_bytes(a.pps, a.page, G));
   dim3 grid(splits, a.hkv, batch);
   const int u = tune_decode_batch(mode);
   if (u == 4)

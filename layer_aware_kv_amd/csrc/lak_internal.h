@@ -31,10 +31,13 @@ struct DecodeArgs {
   // outputs
   float* o_part;               // [B][Hq][s_cap][D]
   float* ml_part;              // [B][Hq][s_cap][2]  (max in log2 units, sum)
-  float* logits;               // delta tier: [B][Hkv][t_pad/16][Gp][16] (Gp = G rounded up to even)
-  int lds_logits;              // delta tier: stage logits in LDS and write them at the split's end
-  int sum_pairs;               // delta tier with SUM aggregation: write per (head, sub-tile) the
-                               // pair (max logit in log2 units, sum of 2^(logit - max)) instead of logits
+  // delta tier, MAX aggregation: per (b, g, 16-token sub-tile, head) the head's max logit r
+  // over the sub-tile (log2 units) and every token's relative weight 2^(logit - r) in fp16:
+  uint16_t* rel_w;             // [B][Hkv][t_pad/16][Gp][16] fp16 (Gp = G rounded up to even)
+  float* rel_max;              // [B][Hkv][t_pad/16][Gp]
+  int lds_logits;              // delta tier: stage them in LDS and write them at the split's end
+  float* logits;               // delta tier, SUM aggregation: per (head, sub-tile) the pair
+  int sum_pairs;               // (max logit in log2 units, sum of 2^(logit - max)) [..][Gp][2]
   int64_t t_pad;               // token capacity of a sequence (max_pages * page)
 };
 
@@ -52,7 +55,9 @@ struct CombineArgs {
 };
 
 struct PageScoreArgs {
-  const float* logits;        // [B][Hkv][t_pad/16][Gp][16], as written by the decode kernel
+  const uint16_t* rel_w;      // MAX: relative weights and sub-tile maxima as the decode kernel
+  const float* rel_max;       //      wrote them (DecodeArgs::rel_w, rel_max)
+  const float* logits;        // SUM: (max, sum) pairs
   const float* lse;           // [B][Hq]
   const int32_t* seq_lens;
   float* scores;              // [B][R][max_pages]
@@ -94,9 +99,15 @@ struct KvGeom {
 //   LAK_TUNE_SPARSE_BATCH  the same for the sparse tier (1, 2 or 4)
 //   LAK_TUNE_TARGET_WGS    workgroups a full / delta split-K launch aims for
 //   LAK_TUNE_SPARSE_WGS    workgroups a sparse split-K launch aims for
-//   LAK_TUNE_DELTA_WGS     workgroups a delta split-K launch aims for
+//   LAK_TUNE_DELTA_WGS     workgroups a delta split-K launch aims for (default 1536)
 //   LAK_TUNE_DELTA_LDS     1 (default): delta logits staged in LDS, written at a split's end
 int tune_decode_batch(int mode);
+
+// LDS bytes of a delta split's staged blocks (fp16 weights + float maxima per sub-tile).
+inline size_t delta_stage_bytes(int pps, int page, int G) {
+  const size_t gp = (size_t)(G + (G & 1));
+  return (size_t)pps * (page / 16) * gp * (16 * 2 + 4);
+}
 int tune_target_wgs(int mode);
 int tune_delta_lds();
 

@@ -12,8 +12,10 @@ namespace lak {
 // One block = `tokens_per_block` consecutive tokens of one score row; each thread
 // takes 4 consecutive tokens, so a page of P tokens is P/4 adjacent lanes and its
 // sum is a butterfly over them (fixed order: scores are bitwise reproducible).
-// Logits come in the decode kernel's blocks: per (b, KV head g, 16-token sub-tile)
-// [Gp heads][16 tokens], Gp = G rounded up to even.
+// Input: the decode kernel's blocks per (b, KV head g, 16-token sub-tile): [Gp heads]
+// [16 tokens] fp16 weights u relative to the head's sub-tile max r (log2 units), and
+// the maxima [Gp].  Token weight of head h: u * 2^(r - lse_h log2 e), the softmax
+// weight exp(logit - lse_h) up to the fp16 rounding of u.
 template <int P>
 __global__ __launch_bounds__(256) void page_score_kernel(PageScoreArgs a) {
   static_assert(P % 16 == 0 && P / 4 <= 64, "page of 16..256 tokens");
@@ -31,34 +33,26 @@ __global__ __launch_bounds__(256) void page_score_kernel(PageScoreArgs a) {
   float* out = a.scores + ((int64_t)b * rows + r) * a.max_pages;
   const int tb0 = chunk * a.tokens_per_block;
   const int tb1 = min(tb0 + a.tokens_per_block, t_end);
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   for (int base = tb0; base < tb1; base += 4 * blockDim.x) {
     const int t = base + 4 * threadIdx.x;  // first of this thread's 4 tokens
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     if (t < tb1) {
       for (int g = g_lo; g < g_hi; ++g) {
-        const float* bp = a.logits + (((int64_t)b * a.hkv + g) * nsub + t / 16) * Gp * 16 + (t % 16);
-        int h = 0;
-        for (; h + 4 <= G; h += 4) {
-          f32x4 v[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4*>(bp + (h + u) * 16);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float lse = ls[g * G + h + u];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float w = (t + e < T) ? expf(v[u][e] - lse) : 0.f;
-              acc[e] = (a.agg == 0) ? fmaxf(acc[e], w) : acc[e] + w;
-            }
-          }
-        }
-        for (; h < G; ++h) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(bp + h * 16);
-          const float lse = ls[g * G + h];
+        const int64_t blk = ((int64_t)b * a.hkv + g) * nsub + t / 16;
+        const uint16_t* up = a.rel_w + blk * Gp * 16 + (t % 16);
+        const float* rp = a.rel_max + blk * Gp;
+        for (int h = 0; h < G; ++h) {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(up + h * 16);
+          const float c = exp2f(rp[h] - ls[g * G + h] * kLog2e);
+          const float u[4] = {(float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] & 0xFFFFu)),
+                              (float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] >> 16)),
+                              (float)__builtin_bit_cast(_Float16, (uint16_t)(w[1] & 0xFFFFu)),
+                              (float)__builtin_bit_cast(_Float16, (uint16_t)(w[1] >> 16))};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float w = (t + e < T) ? expf(v[e] - lse) : 0.f;
-            acc[e] = (a.agg == 0) ? fmaxf(acc[e], w) : acc[e] + w;
+            const float x = (t + e < T) ? u[e] * c : 0.f;
+            acc[e] = (a.agg == 0) ? fmaxf(acc[e], x) : acc[e] + x;
           }
         }
       }

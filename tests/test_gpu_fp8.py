@@ -120,7 +120,8 @@ def test_fp8_delta_select_and_sparse(spec, agg, scope):
         r = oracle.delta_layer(case.q[b], K, V, sm, P, k_top, rec, agg, scope)
         NP = -(-T // P)
         got = scores[b].cpu().numpy().astype(np.float64)
-        np.testing.assert_allclose(got[:, :NP], r["page_scores"], rtol=1e-4, atol=1e-7)
+        # MAX: fp16 weights relative to each (head, sub-tile) maximum, relative error <= 2^-11
+        np.testing.assert_allclose(got[:, :NP], r["page_scores"], rtol=6e-4 if agg == "max" else 1e-4, atol=1e-7)
         for row in range(R):
             check_selection(sel[b, row].cpu().numpy(), int(cnt[b, row]), r["page_scores"][row], k_top, rec,
                             sel.shape[-1])
@@ -164,7 +165,7 @@ def test_fp8_zero_rows_and_write_rows():
     _check_codes(cache, case)
     ks, vs = cache.kv_gather_scales(0, 1, 1, 200, 1)
     assert float(vs[0]) == 0.0
-    # single-row overwrite re-encodes the row (keys only for the second row: v_rows NULL)
+    # single-row overwrite re-encodes the K and V rows (the out-of-range third row is skipped)
     rows = torch.tensor([[1, 0, 17], [0, 1, 3], [1, 1, 10 ** 6]], dtype=torch.int32, device="cuda")
     new = random_case(9, 1, 8, 3, 64, [1], "bf16").K[0, :, 0]  # 3 rows of 64
     kr = to_dev(new, "bf16")

@@ -42,6 +42,9 @@ def _case(spec, seed=11):
     return c, P, float(scale)
 
 
+SCORE_RTOL = {"max": 6e-4, "sum": 1e-4}
+
+
 def _budget(T, P):
     NP = -(-T // P)
     return max(1, NP // 5), 2
@@ -84,7 +87,9 @@ def test_delta_select(spec, agg, scope):
         NP = -(-T // P)
         S = r["page_scores"]
         got = scores[b].cpu().numpy().astype(np.float64)
-        np.testing.assert_allclose(got[:, :NP], S, rtol=1e-4, atol=1e-7)
+        # MAX scores come from fp16 weights relative to each (head, sub-tile) maximum:
+        # relative error <= 2^-11; SUM scores from exact (max, sum) pairs
+        np.testing.assert_allclose(got[:, :NP], S, rtol=SCORE_RTOL[agg], atol=1e-7)
         assert np.all(got[:, NP:] == -7.0)  # entries past NP untouched
         for row in range(R):
             check_selection(sel[b, row].cpu().numpy(), int(cnt[b, row]), S[row], k_top, rec, sel.shape[-1])

@@ -84,7 +84,9 @@ def test_single_layer_workload_full_delta_sparse(index):
         assert_close(host(lse_f[0]), ref["lse"], LSE_TOL[wl.dtype], "lse")
         assert torch.equal(out_d, out_f)
         NP = -(-T // wl.page)
-        np.testing.assert_allclose(scores[0, :, :NP].cpu().numpy(), ref["page_scores"], rtol=1e-4, atol=1e-7)
+        # MAX: fp16 weights relative to each (head, sub-tile) maximum, relative error <= 2^-11
+        np.testing.assert_allclose(scores[0, :, :NP].cpu().numpy(), ref["page_scores"],
+                                   rtol=6e-4 if agg == "max" else 1e-4, atol=1e-7)
         for g in range(wl.hkv):
             check_selection(sel[0, g].cpu().numpy(), int(cnt[0, g]), ref["page_scores"][g], wl.k_top, wl.recency,
                             sel.shape[-1])
