@@ -475,7 +475,9 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
 
   // U sub-tiles per batch: their loads are issued together (unconditionally, so
   // the wait before each sub-tile is exact) and consumed in order; other waves of
-  // the CU cover the latency between batches.
+  // the CU cover the latency between batches.  (A two-buffer pipeline that keeps
+  // the next sub-tile's loads in flight during the math measured slower: it costs
+  // occupancy, and occupancy hides the latency better.)
   for (int x = 0; x < nsub; x += U) {
     F buf[U];
     Sub info[U];
@@ -536,26 +538,28 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-    const int hn = idx / D, d = idx - hn * D;
+  // 4 consecutive head-dim elements per thread (one pass for G * D <= 1024): the
+  // waves' weights are taken once per 4 elements and the partial row is written in
+  // 16-byte stores.
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  for (int idx = threadIdx.x; idx < G * D / 4; idx += blockDim.x) {
+    const int hn = (4 * idx) / D, d = 4 * idx - hn * D;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lm[w * 16 + hn]);
-    float acc = 0.f, L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float f = exp2f(lm[w * 16 + hn] - M);
-        acc += f * lo[(w * G + hn) * D + d];
+        acc += f * *reinterpret_cast<const f32x4*>(lo + (w * G + hn) * D + d);
         L += f * ll[w * 16 + hn];
       }
     }
     const int64_t row = ((int64_t)b * a.hq + g * G + hn) * a.s_cap + s;
-    a.o_part[row * D + d] = acc;
-    if (d == 0) {
-      a.ml_part[row * 2] = M;
-      a.ml_part[row * 2 + 1] = L;
-    }
+    *reinterpret_cast<f32x4*>(a.o_part + row * D + d) = acc;
+    if (d == 0) *reinterpret_cast<f32x2*>(a.ml_part + row * 2) = (f32x2){M, L};
   }
 }
 
