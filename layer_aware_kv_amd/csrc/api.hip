@@ -79,6 +79,11 @@ int lak::tune_target_wgs(int mode) {
   return mode == MODE_SPARSE ? sparse : (mode == MODE_DELTA ? delta : full);
 }
 
+int lak::tune_min_subtiles() {
+  static const int v = env_int("LAK_TUNE_MIN_SUBTILES", kMinSubtilesPerWg, 1, 256);
+  return v;
+}
+
 int lak::tune_delta_lds() {
   static const int v = env_int("LAK_TUNE_DELTA_LDS", 1, 0, 1);
   return v;
@@ -156,7 +161,8 @@ int plan_pps(int rows, int max_items, int subtiles_per_page, int mode) {
   const int64_t work = (int64_t)rows * max_items;
   const int target = tune_target_wgs(mode);
   int pps = (int)((work + target - 1) / target);
-  const int min_pps = (kMinSubtilesPerWg + subtiles_per_page - 1) / subtiles_per_page;
+  const int min_sub = tune_min_subtiles();
+  const int min_pps = (min_sub + subtiles_per_page - 1) / subtiles_per_page;
   return std::min(std::max(std::max(pps, min_pps), 1), kMaxItemsPerSplit);
 }
 

@@ -100,7 +100,8 @@ struct KvGeom {
 //   LAK_TUNE_TARGET_WGS    workgroups a full / delta split-K launch aims for
 //   LAK_TUNE_SPARSE_WGS    workgroups a sparse split-K launch aims for
 //   LAK_TUNE_DELTA_WGS     workgroups a delta split-K launch aims for (default 1536)
-//   LAK_TUNE_DELTA_LDS     1 (default): delta logits staged in LDS, written at a split's end
+//   LAK_TUNE_DELTA_LDS     1 (default): delta scratch staged in LDS, written at a split's end
+//   LAK_TUNE_MIN_SUBTILES  fewest 16-token sub-tiles a split-K workgroup is given (default 8)
 int tune_decode_batch(int mode);
 
 // LDS bytes of a delta split's staged blocks (fp16 weights + float maxima per sub-tile).
@@ -110,6 +111,7 @@ inline size_t delta_stage_bytes(int pps, int page, int G) {
 }
 int tune_target_wgs(int mode);
 int tune_delta_lds();
+int tune_min_subtiles();
 
 // launchers (return hipSuccess or the launch error)
 hipError_t launch_decode(int dtype, int mode, int D, const DecodeArgs& a, int splits, int batch,

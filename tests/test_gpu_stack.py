@@ -85,7 +85,8 @@ def test_stack_full_size_sampled(index, kv):
     print(f"{wl.name}: {n_band} selected pages differ inside the boundary band", flush=True)
 
 
-def test_native_stack_step_equals_python_loop():
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_native_stack_step_equals_python_loop(kv):
     """lak_stack_step (schedule in C++) gives the same bits as the per-layer calls."""
     from layer_aware_kv_amd import DeltaStack, LakError, PagedKVCache
     from workload.cases import random_case
@@ -95,7 +96,7 @@ def test_native_stack_step_equals_python_loop():
     steps = 5
     runs = []
     for native in (True, False):
-        cache = PagedKVCache(L, B, HQ, HKV, D, P, 64, 3 * 64, "bf16")
+        cache = PagedKVCache(L, B, HQ, HKV, D, P, 64, 3 * 64, kv)
         cache.seq_reset(lens, reserve_tokens=steps)
         for layer in range(L):
             c = random_case(100 + layer, B, HQ, HKV, D, lens, "bf16")
