@@ -123,7 +123,7 @@ struct lak_cache {
 namespace {
 
 struct WsLayout {
-  size_t o_part, ml_part, lse, logits, rel_max, scores, total;
+  size_t o_part, ml_part, lse, delta, rel_max, scores, total;
 };
 
 WsLayout ws_layout(const lak_cache* c) {
@@ -142,7 +142,7 @@ WsLayout ws_layout(const lak_cache* c) {
   // delta scratch: fp16 relative weights [B][Hkv][sub-tiles][Gp][16] (MAX) or the
   // (max, sum) pairs [B][Hkv][sub-tiles][Gp][2] float (SUM), then the sub-tile maxima
   // [B][Hkv][sub-tiles][Gp] float (MAX); Gp = G rounded up to even
-  w.logits = off;
+  w.delta = off;
   const int G = d.num_q_heads / d.num_kv_heads;
   const size_t gp = (size_t)(G + (G & 1));
   const size_t blocks = (size_t)d.max_batch * d.num_kv_heads * gp * ((size_t)d.max_pages_per_seq * d.page_size / 16);
@@ -250,13 +250,13 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
   a.sel_rows = sel_rows;
   a.o_part = reinterpret_cast<float*>(wsb + w.o_part);
   a.ml_part = reinterpret_cast<float*>(wsb + w.ml_part);
-  a.logits = reinterpret_cast<float*>(wsb + w.logits);
-  a.rel_w = reinterpret_cast<uint16_t*>(wsb + w.logits);
+  a.pairs = reinterpret_cast<float*>(wsb + w.delta);
+  a.rel_w = reinterpret_cast<uint16_t*>(wsb + w.delta);
   a.rel_max = reinterpret_cast<float*>(wsb + w.rel_max);
   {
     const int G = d.num_q_heads / d.num_kv_heads;
     const size_t staged = delta_stage_bytes(pps, d.page_size, G);
-    a.lds_logits = (mode == MODE_DELTA && tune_delta_lds() && staged <= 64 * 1024) ? 1 : 0;
+    a.lds_stage = (mode == MODE_DELTA && tune_delta_lds() && staged <= 64 * 1024) ? 1 : 0;
     a.sum_pairs = (mode == MODE_DELTA && agg == LAK_AGG_SUM) ? 1 : 0;
   }
   a.t_pad = (int64_t)d.max_pages_per_seq * d.page_size;
@@ -602,8 +602,8 @@ lak_status lak_attn_delta_select(lak_cache* c, int32_t layer, const void* q, con
   char* wsb = static_cast<char*>(ws);
   float* scores = page_scores ? page_scores : reinterpret_cast<float*>(wsb + w.scores);
   PageScoreArgs pa;
-  pa.logits = reinterpret_cast<const float*>(wsb + w.logits);
-  pa.rel_w = reinterpret_cast<const uint16_t*>(wsb + w.logits);
+  pa.pairs = reinterpret_cast<const float*>(wsb + w.delta);
+  pa.rel_w = reinterpret_cast<const uint16_t*>(wsb + w.delta);
   pa.rel_max = reinterpret_cast<const float*>(wsb + w.rel_max);
   pa.lse = reinterpret_cast<const float*>(wsb + w.lse);
   pa.seq_lens = c->d.seq_lens;

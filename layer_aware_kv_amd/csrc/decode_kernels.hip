@@ -8,11 +8,12 @@
 //               aggregation), or the (max, sum of exponentials) pair (SUM),
 //   MODE_SPARSE attention over the tokens of the selected pages only.
 // One workgroup = one (sequence b, KV head g, split s); a row's pages are dealt to
-// its splits round-robin and a split's 4 waves take its pages in turn.  Per sub-tile: S^T = K Q^T with the G query heads
-// of the group as the 16-wide MFMA N dimension, online softmax in the log2
-// domain, then O^T += V^T P^T.  K and V fragments come straight from HBM into
-// registers (the pool's in-page order matches the MFMA operand layout, so every
-// load instruction is one contiguous 1 KiB).  Waves merge through LDS; the split
+// its splits round-robin and a split's 4 waves take its pages in turn.  Per
+// sub-tile: S^T = K Q^T with the G query heads of the group as the 16-wide MFMA N
+// dimension, online softmax in the log2 domain, then O^T += V^T P^T.  K and V
+// fragments come straight from HBM into registers (the pool's in-page order matches
+// the MFMA operand layout, so every load instruction is one contiguous 1 KiB); fp8
+// pools are widened to bfloat16 in registers.  Waves merge through LDS; the split
 // partials (o, max, sum) are merged by combine_kernel.
 #include <math.h>
 
@@ -25,7 +26,7 @@ namespace lak {
 
 // 16-byte fragment load.  STREAM marks it non-temporal: the K/V stream of a full
 // pass (gigabytes) then does not evict from the caches what is reused soon (the
-// delta-layer logits, the page table, the partials).
+// delta-layer scratch, the page table, the partials).
 template <bool STREAM>
 __device__ inline u32x4 load16(const u32x4* p) {
   if (STREAM) return __builtin_nontemporal_load(p);
@@ -435,7 +436,7 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
       if (head_ok && j == 0) {
         const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + ct / kSub;
         typedef float f32x2 __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<f32x2*>(a.logits + (blk * Gp + n) * 2) = (f32x2){mx, e};
+        *reinterpret_cast<f32x2*>(a.pairs + (blk * Gp + n) * 2) = (f32x2){mx, e};
       }
     } else if (MODE == MODE_DELTA && n < Gp) {
       // MAX aggregation: this head's max logit r over the sub-tile (log2 units, exact)
@@ -453,7 +454,7 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
       }
       const float rmax = head_ok ? mx : 0.f;
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      if (a.lds_logits) {
+      if (a.lds_stage) {
         // staged in LDS at the sub-tile's index within the workgroup; flushed at the end
         const int li = (wave + kWaves * (x / spp)) * spp + (x % spp);
         uint16_t* lu = reinterpret_cast<uint16_t*>(lds);
@@ -491,7 +492,7 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
       if (info[u].valid) process(buf[u], info[u].t0, x + u);
   }
 
-  if (MODE == MODE_DELTA && a.lds_logits && !a.sum_pairs) {
+  if (MODE == MODE_DELTA && a.lds_stage && !a.sum_pairs) {
     // write the workgroup's blocks in one burst: 16-byte units of fp16 weights (two per
     // head row), then the maxima
     __syncthreads();
@@ -653,7 +654,7 @@ static hipError_t launch_decode_t(int mode, const DecodeArgs& a, int splits, int
                                   hipStream_t st) {
   const int G = a.hq / a.hkv;
   size_t lds = (size_t)(kWaves * G * D + 2 * kWaves * 16) * sizeof(float);
-  if (mode == MODE_DELTA && a.lds_logits && !a.sum_pairs)
+  if (mode == MODE_DELTA && a.lds_stage && !a.sum_pairs)
     lds = std::max(lds, delta_stage_bytes(a.pps, a.page, G));
   dim3 grid(splits, a.hkv, batch);
   const int u = tune_decode_batch(mode);

@@ -35,8 +35,8 @@ struct DecodeArgs {
   // over the sub-tile (log2 units) and every token's relative weight 2^(logit - r) in fp16:
   uint16_t* rel_w;             // [B][Hkv][t_pad/16][Gp][16] fp16 (Gp = G rounded up to even)
   float* rel_max;              // [B][Hkv][t_pad/16][Gp]
-  int lds_logits;              // delta tier: stage them in LDS and write them at the split's end
-  float* logits;               // delta tier, SUM aggregation: per (head, sub-tile) the pair
+  int lds_stage;               // delta tier: stage them in LDS and write them at the split's end
+  float* pairs;                // delta tier, SUM aggregation: per (head, sub-tile) the pair
   int sum_pairs;               // (max logit in log2 units, sum of 2^(logit - max)) [..][Gp][2]
   int64_t t_pad;               // token capacity of a sequence (max_pages * page)
 };
@@ -57,7 +57,7 @@ struct CombineArgs {
 struct PageScoreArgs {
   const uint16_t* rel_w;      // MAX: relative weights and sub-tile maxima as the decode kernel
   const float* rel_max;       //      wrote them (DecodeArgs::rel_w, rel_max)
-  const float* logits;        // SUM: (max, sum) pairs
+  const float* pairs;         // SUM: (max, sum) pairs
   const float* lse;           // [B][Hq]
   const int32_t* seq_lens;
   float* scores;              // [B][R][max_pages]

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void page_score_pairs_kernel(PageScoreArgs a) 
     for (int u = 0; u < spp; ++u) {
       const int st = jp * spp + u;
       if (st * 16 >= T) break;
-      const float* pp = a.logits + ((((int64_t)b * a.hkv + g) * nsub + st) * Gp) * 2;
+      const float* pp = a.pairs + ((((int64_t)b * a.hkv + g) * nsub + st) * Gp) * 2;
       for (int h = 0; h < G; ++h) acc += pp[2 * h + 1] * expf(pp[2 * h] * kLn2 - ls[g * G + h]);
     }
   }
