@@ -220,13 +220,6 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
   std::memset(&a, 0, sizeof(a));
   hipError_t e = hipSuccess;
   if (d.dtype == LAK_FP8_E4M3) {
-    // fp8 rows are encoded with a per-row scale by the append kernel first (the
-    // decode kernel then reads the token from the pool like any other)
-    if (k_new) {
-      e = launch_append(geom(c), c->kp[layer], c->vp[layer], d.page_table, d.seq_lens, k_new, v_new, c->batch, st);
-      if (e != hipSuccess) return hip_fail(e, "append launch");
-    }
-    k_new = v_new = nullptr;
     a.k_scale = reinterpret_cast<const float*>(static_cast<const char*>(c->kp[layer]) + code_bytes(d));
     a.v_scale = reinterpret_cast<const float*>(static_cast<const char*>(c->vp[layer]) + code_bytes(d));
   }

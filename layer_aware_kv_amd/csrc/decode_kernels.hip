@@ -302,21 +302,28 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
   }
   // Fused append: split 0 of each (b, g) writes this step's token at T-1 into the
   // pool for later calls; the wave that attends over that sub-tile in this call
-  // takes the token from k_new / v_new directly (see `patch` below).
-  const E* krow_new = nullptr;
-  const E* vrow_new = nullptr;
-  if (ESZ != 1 && a.k_new != nullptr && T > 0) {
-    krow_new = reinterpret_cast<const E*>(a.k_new) + ((int64_t)b * a.hkv + g) * D;
-    vrow_new = reinterpret_cast<const E*>(a.v_new) + ((int64_t)b * a.hkv + g) * D;
+  // takes the token from k_new / v_new directly (`patch`; fp8 pools: see `issue`).
+  // (fp8 pools: rows arrive as bfloat16 and are encoded with their row scale.)
+  const QE* krow_new = nullptr;
+  const QE* vrow_new = nullptr;
+  if (a.k_new != nullptr && T > 0) {
+    krow_new = reinterpret_cast<const QE*>(a.k_new) + ((int64_t)b * a.hkv + g) * D;
+    vrow_new = reinterpret_cast<const QE*>(a.v_new) + ((int64_t)b * a.hkv + g) * D;
     if (s == 0) {
       const int t = T - 1;
       const int64_t phys = a.page_table[(int64_t)b * a.max_pages + t / P];
-      const int64_t base = ((phys * a.hkv + g) * P + ((t % P) / kSub) * kSub) * (int64_t)D;
+      const int64_t row0 = (phys * a.hkv + g) * P + ((t % P) / kSub) * kSub;  // sub-tile's first row
       E* kp = const_cast<E*>(reinterpret_cast<const E*>(a.k_pool));
       E* vp = const_cast<E*>(reinterpret_cast<const E*>(a.v_pool));
-      for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        kp[base + k_off<ESZ>(t % kSub, d)] = krow_new[d];
-        vp[base + v_off<ESZ>(t % kSub, d)] = vrow_new[d];
+      if constexpr (ESZ == 1) {
+        if (threadIdx.x < 64)
+          encode_rows_fp8(D, kp + row0 * D, vp + row0 * D, t % kSub, const_cast<float*>(a.k_scale) + row0 + t % kSub,
+                          const_cast<float*>(a.v_scale) + row0 + t % kSub, krow_new, vrow_new, threadIdx.x);
+      } else {
+        for (int d = threadIdx.x; d < D; d += blockDim.x) {
+          kp[row0 * D + k_off<ESZ>(t % kSub, d)] = krow_new[d];
+          vp[row0 * D + v_off<ESZ>(t % kSub, d)] = vrow_new[d];
+        }
       }
     }
   }
@@ -362,6 +369,27 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
   // The ids (and q) are in registers before the loop: wait for them once here, so
   // that reading them inside the loop never waits on the K/V loads in flight.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+  if constexpr (ESZ == 1) {
+    // fp8 fused append: the wave whose items include the page of this step's token
+    // encodes and stores that row itself (the same bytes split 0 writes) before any
+    // of its loads, so it then reads the token from the pool like any other; the
+    // workgroup-scope fence orders its lanes' stores before those loads.
+    if (krow_new != nullptr) {
+      const unsigned long long own = __ballot(lane < n_w && lp_vec == (T - 1) / P);
+      if (own != 0ull) {
+        const int64_t phys = __builtin_amdgcn_readlane(pid_vec, __ffsll(own) - 1);
+        const int tin = (T - 1) % P;
+        const int64_t row0 = (phys * a.hkv + g) * P + (tin / kSub) * kSub;
+        const int tt = tin % kSub;
+        encode_rows_fp8(D, const_cast<E*>(kpool) + row0 * D, const_cast<E*>(vpool) + row0 * D, tt,
+                        const_cast<float*>(a.k_scale) + row0 + tt, const_cast<float*>(a.v_scale) + row0 + tt,
+                        krow_new, vrow_new, lane);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      }
+    }
+  }
 
   struct Sub {
     bool valid;

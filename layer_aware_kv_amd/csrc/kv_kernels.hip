@@ -135,21 +135,7 @@ __device__ inline float* scale_ptr(uint8_t* pool, const KvGeom& g) {
 // at `base` (token tt of the sub-tile) and stores their scales at scale index si.
 __device__ inline void encode_row_fp8(const KvGeom& g, uint8_t* kp, uint8_t* vp, int64_t base, int tt,
                                       int64_t si, const uint16_t* kr, const uint16_t* vr, int lane) {
-  float ka = 0.f, va = 0.f;
-  for (int d = lane; d < g.d; d += 64) {
-    ka = fmaxf(ka, fabsf(bf16_to_f32(kr[d])));
-    if (vr) va = fmaxf(va, fabsf(bf16_to_f32(vr[d])));
-  }
-  const float ksc = e4m3_row_scale(wave_max(ka));
-  const float vsc = e4m3_row_scale(wave_max(va));
-  for (int d = lane; d < g.d; d += 64) {
-    kp[base + k_off<1>(tt, d)] = (uint8_t)(e4m3_encode2(bf16_to_f32(kr[d]), 0.f, ksc) & 0xFFu);
-    if (vr) vp[base + v_off<1>(tt, d)] = (uint8_t)(e4m3_encode2(bf16_to_f32(vr[d]), 0.f, vsc) & 0xFFu);
-  }
-  if (lane == 0) {
-    scale_ptr(kp, g)[si] = ksc;
-    if (vr) scale_ptr(vp, g)[si] = vsc;
-  }
+  encode_rows_fp8(g.d, kp + base, vp + base, tt, scale_ptr(kp, g) + si, scale_ptr(vp, g) + si, kr, vr, lane);
 }
 
 __global__ void append_fp8_kernel(KvGeom g, uint8_t* kp, uint8_t* vp, const int32_t* pt, const int32_t* lens,

@@ -87,6 +87,30 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
+// Row scale of a bfloat16 row of d values taken by one whole wave (every lane
+// calls it; the maximum is order-independent, so every caller gets the same bits).
+__device__ inline float e4m3_wave_row_scale(const uint16_t* row, int d, int lane) {
+  float m = 0.f;
+  for (int i = lane; i < d; i += 64) m = fmaxf(m, fabsf(bf16_to_f32(row[i])));
+  return e4m3_row_scale(wave_max(m));
+}
+
+// One wave encodes token tt's K row and V row (d bfloat16 values each; vr may be
+// NULL) into the fp8 sub-tiles at kb / vb and stores the scales at *ks / *vs.
+__device__ inline void encode_rows_fp8(int d, uint8_t* kb, uint8_t* vb, int tt, float* ks, float* vs,
+                                       const uint16_t* kr, const uint16_t* vr, int lane) {
+  const float ksc = e4m3_wave_row_scale(kr, d, lane);
+  const float vsc = vr ? e4m3_wave_row_scale(vr, d, lane) : 0.f;
+  for (int i = lane; i < d; i += 64) {
+    kb[k_off<1>(tt, i)] = (uint8_t)(e4m3_encode2(bf16_to_f32(kr[i]), 0.f, ksc) & 0xFFu);
+    if (vr) vb[v_off<1>(tt, i)] = (uint8_t)(e4m3_encode2(bf16_to_f32(vr[i]), 0.f, vsc) & 0xFFu);
+  }
+  if (lane == 0) {
+    *ks = ksc;
+    if (vr) *vs = vsc;
+  }
+}
+
 // Inclusive prefix sum over a wave (64 lanes).
 __device__ inline int wave_incl_scan(int v, int lane) {
 #pragma unroll

@@ -16,7 +16,7 @@ struct DecodeArgs {
   const int32_t* seq_lens;     // [max_batch]
   const void* q;               // [B][Hq][D]
   const void* k_new;           // optional [B][Hkv][D]: token appended at T-1 by this call
-  const void* v_new;           // (never set for fp8 pools: their append is a separate launch)
+  const void* v_new;           // (bfloat16 rows for fp8 pools, encoded by the kernel)
   const float* k_scale;        // fp8 pools: per-token scales [page][Hkv][P] after the codes
   const float* v_scale;
   float sm_scale;
