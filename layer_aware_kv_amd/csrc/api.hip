@@ -42,8 +42,11 @@ constexpr int kTargetWgs = 1024;
 constexpr int kTargetWgsDelta = 1536;  // smaller delta splits spread the scratch writes
 constexpr int kMinSubtilesPerWg = 8;
 // Each of the 4 waves of a decode workgroup keeps the page ids of its items in one
-// register per lane, so a split holds at most 4 * 64 items.
+// register per lane (two for the full tier), so a split holds at most 4 * 64 items
+// (4 * 128).  The full tier's wider cap keeps a one-page-longer context at one
+// workgroup round (4097 pages: 16 splits of 257 instead of 17 of 256).
 constexpr int kMaxItemsPerSplit = 256;
+constexpr int kMaxItemsPerSplitFull = 512;
 constexpr int kScoreTokensPerBlock = 2048;
 
 int esize(int dtype) { return dtype == LAK_BF16 ? 2 : (dtype == LAK_FP8_E4M3 ? 1 : 4); }
@@ -163,7 +166,7 @@ int plan_pps(int rows, int max_items, int subtiles_per_page, int mode) {
   int pps = (int)((work + target - 1) / target);
   const int min_sub = tune_min_subtiles();
   const int min_pps = (min_sub + subtiles_per_page - 1) / subtiles_per_page;
-  return std::min(std::max(std::max(pps, min_pps), 1), kMaxItemsPerSplit);
+  return std::min(std::max(std::max(pps, min_pps), 1), mode == MODE_FULL ? kMaxItemsPerSplitFull : kMaxItemsPerSplit);
 }
 
 lak_status check_cache(const lak_cache* c, bool need_device) {

@@ -351,20 +351,35 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
   const int spp = P / kSub;
   const float qk_scale2 = a.sm_scale * kLog2e;
 
-  // This wave takes members wave + kWaves*k (k < n_w <= 64: the host caps the items
-  // per split) of its split.  Lane k fetches the logical and physical page of its item
-  // once; each sub-tile then reads them with v_readlane (no memory access in the loop).
+  // This wave takes members wave + kWaves*k (k < n_w <= 64 * kIdRegs: the host caps
+  // the items per split at 256, 512 for the full tier) of its split.  Lane k % 64
+  // fetches the logical and physical page of item k once into register k / 64; each
+  // sub-tile then reads them with v_readlane (no memory access in the loop).
+  constexpr int kIdRegs = (MODE == MODE_FULL) ? 2 : 1;
   const int n_w = max(0, (n_split - wave + kWaves - 1) / kWaves);
   const int nsub = n_w * spp;
-  int lp_vec = -1, pid_vec = 0;
-  if (lane < n_w) {
-    const int it = s + S_row * (wave + kWaves * lane);
-    int lp = (MODE == MODE_SPARSE) ? sel_row[it] : it;
-    if (lp >= 0 && lp < NP) {
-      lp_vec = lp;
-      pid_vec = ptab[lp];
+  int lp_vec[kIdRegs], pid_vec[kIdRegs];
+#pragma unroll
+  for (int r = 0; r < kIdRegs; ++r) {
+    lp_vec[r] = -1;
+    pid_vec[r] = 0;
+    if (lane + 64 * r < n_w) {
+      const int it = s + S_row * (wave + kWaves * (lane + 64 * r));
+      int lp = (MODE == MODE_SPARSE) ? sel_row[it] : it;
+      if (lp >= 0 && lp < NP) {
+        lp_vec[r] = lp;
+        pid_vec[r] = ptab[lp];
+      }
     }
   }
+  auto item_lp = [&](int k) -> int {
+    return (kIdRegs == 1 || k < 64) ? __builtin_amdgcn_readlane(lp_vec[0], k & 63)
+                                    : __builtin_amdgcn_readlane(lp_vec[kIdRegs - 1], k & 63);
+  };
+  auto item_pid = [&](int k) -> int {
+    return (kIdRegs == 1 || k < 64) ? __builtin_amdgcn_readlane(pid_vec[0], k & 63)
+                                    : __builtin_amdgcn_readlane(pid_vec[kIdRegs - 1], k & 63);
+  };
 
   // The ids (and q) are in registers before the loop: wait for them once here, so
   // that reading them inside the loop never waits on the K/V loads in flight.
@@ -376,9 +391,18 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
     // of its loads, so it then reads the token from the pool like any other; the
     // workgroup-scope fence orders its lanes' stores before those loads.
     if (krow_new != nullptr) {
-      const unsigned long long own = __ballot(lane < n_w && lp_vec == (T - 1) / P);
+      unsigned long long own = 0ull;
+      int k_own = 0;
+#pragma unroll
+      for (int r = kIdRegs - 1; r >= 0; --r) {
+        const unsigned long long o = __ballot(lp_vec[r] == (T - 1) / P);
+        if (o != 0ull) {
+          own = o;
+          k_own = 64 * r + __ffsll(o) - 1;
+        }
+      }
       if (own != 0ull) {
-        const int64_t phys = __builtin_amdgcn_readlane(pid_vec, __ffsll(own) - 1);
+        const int64_t phys = item_pid(k_own);
         const int tin = (T - 1) % P;
         const int64_t row0 = (phys * a.hkv + g) * P + (tin / kSub) * kSub;
         const int tt = tin % kSub;
@@ -401,10 +425,10 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
   auto issue = [&](F& f, int x) -> Sub {
     const int k = x / spp;
     const int sub = x - k * spp;
-    const int lp = __builtin_amdgcn_readlane(lp_vec, k);
+    const int lp = item_lp(k);
     const int t0 = lp * P + sub * kSub;
     const bool valid = lp >= 0 && t0 < T;
-    const int64_t phys = __builtin_amdgcn_readlane(pid_vec, k);
+    const int64_t phys = item_pid(k);
     const int64_t row0 = valid ? (phys * a.hkv + g) * P + sub * kSub : 0;  // first token row
     f.template load<MODE != MODE_SPARSE>(kpool + row0 * D, vpool + row0 * D, a.k_scale + row0,
                                          a.v_scale + row0, lane);
