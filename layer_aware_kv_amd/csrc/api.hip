@@ -158,12 +158,14 @@ WsLayout ws_layout(const lak_cache* c) {
   return w;
 }
 
-// Items (pages or selection entries) per split for `rows` rows of up to
-// `max_items` items each.
-int plan_pps(int rows, int max_items, int subtiles_per_page, int mode) {
-  const int64_t work = (int64_t)rows * max_items;
+// Items (pages or selection entries) per split.  `work` is the total over the call's
+// rows (per-row item counts summed: a ragged batch gives its long rows more splits),
+// `max_items` the longest row's count and `max_splits` the most splits a row may use
+// (the partial buffers hold max_splits per row).
+int plan_pps(int64_t work, int max_items, int max_splits, int subtiles_per_page, int mode) {
   const int target = tune_target_wgs(mode);
   int pps = (int)((work + target - 1) / target);
+  pps = std::max(pps, (max_items + max_splits - 1) / std::max(max_splits, 1));
   const int min_sub = tune_min_subtiles();
   const int min_pps = (min_sub + subtiles_per_page - 1) / subtiles_per_page;
   return std::min(std::max(std::max(pps, min_pps), 1), mode == MODE_FULL ? kMaxItemsPerSplitFull : kMaxItemsPerSplit);
@@ -211,10 +213,16 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
   const WsLayout w = ws_layout(c);
   char* wsb = static_cast<char*>(ws);
   const int spp = d.page_size / 16;
-  int max_items = c->max_np();
-  if (mode == MODE_SPARSE) max_items = std::min(max_items, sel_cap);
-  const int rows = c->batch * d.num_kv_heads;
-  const int pps = plan_pps(rows, max_items, spp, mode);
+  // items per row: the row's pages (a sparse row: at most sel_cap selection entries)
+  int max_items = 0;
+  int64_t work = 0;
+  for (int b = 0; b < c->batch; ++b) {
+    int items = (c->lens[b] + d.page_size - 1) / d.page_size;
+    if (mode == MODE_SPARSE) items = std::min(items, sel_cap);
+    max_items = std::max(max_items, items);
+    work += (int64_t)items * d.num_kv_heads;
+  }
+  const int pps = plan_pps(work, max_items, c->s_cap / std::max(c->batch, 1), spp, mode);
   const int splits = (max_items + pps - 1) / pps;
   if ((int64_t)splits * c->batch > c->s_cap)
     return fail(LAK_EINVAL, "internal: %d splits x %d rows exceed capacity %d", splits, c->batch, c->s_cap);
