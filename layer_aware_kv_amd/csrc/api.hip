@@ -126,22 +126,19 @@ struct lak_cache {
 namespace {
 
 struct WsLayout {
-  size_t o_part, ml_part, lse, delta, rel_max, scores, total;
+  size_t o_part, ml_part, delta, rel_max, scores, total;
 };
 
 WsLayout ws_layout(const lak_cache* c) {
   const auto& d = c->d;
   WsLayout w;
   size_t off = 0;
-  const size_t rows_h = (size_t)d.max_batch * d.num_q_heads;
   // split partials are [B][Hq][S] with S the call's split count: B * S <= s_cap
   const size_t part = (size_t)d.num_q_heads * c->s_cap;
   w.o_part = off;
   off = align256(off + part * d.head_dim * sizeof(float));
   w.ml_part = off;
   off = align256(off + part * 2 * sizeof(float));
-  w.lse = off;
-  off = align256(off + rows_h * sizeof(float));
   // delta scratch: fp16 relative weights [B][Hkv][sub-tiles][Gp][16] (MAX) or the
   // (max, sum) pairs [B][Hkv][sub-tiles][Gp][2] float (SUM), then the sub-tile maxima
   // [B][Hkv][sub-tiles][Gp] float (MAX); Gp = G rounded up to even
@@ -205,10 +202,12 @@ lak_status check_ws(const lak_cache* c, const void* ws, size_t ws_bytes) {
 }
 
 // Runs the split-K decode plus combine of one tier.
+// With `defer_combine` the combine arguments are returned there instead of launched
+// (the delta layer combines inside its page-scoring launch).
 lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const void* k_new,
                          const void* v_new, float sm_scale, void* out, float* lse, const int32_t* sel,
                          const int32_t* sel_count, int sel_cap, int sel_rows, void* ws, hipStream_t st,
-                         int agg = LAK_AGG_MAX) {
+                         int agg = LAK_AGG_MAX, CombineArgs* defer_combine = nullptr) {
   const auto& d = c->d;
   const WsLayout w = ws_layout(c);
   char* wsb = static_cast<char*>(ws);
@@ -285,7 +284,10 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
   cb.splits = splits;
   cb.out = out;
   cb.lse = lse;
-  cb.lse2 = (mode == MODE_DELTA) ? reinterpret_cast<float*>(wsb + w.lse) : nullptr;
+  if (defer_combine) {
+    *defer_combine = cb;
+    return ok();
+  }
   e = launch_combine(d.dtype, d.head_dim, cb, c->batch, st);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ok();
@@ -600,16 +602,17 @@ lak_status lak_attn_delta_select(lak_cache* c, int32_t layer, const void* q, con
   if (c->batch == 0) return ok();
   if ((s = check_ws(c, ws, ws_bytes)) != LAK_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  s = run_attention(c, layer, MODE_DELTA, q, k_new, v_new, sm_scale, out, lse, nullptr, nullptr, 0, 1, ws, st, agg);
+  PageScoreArgs pa;
+  std::memset(&pa, 0, sizeof(pa));
+  s = run_attention(c, layer, MODE_DELTA, q, k_new, v_new, sm_scale, out, lse, nullptr, nullptr, 0, 1, ws, st, agg,
+                    &pa.cb);
   if (s != LAK_OK) return s;
   const WsLayout w = ws_layout(c);
   char* wsb = static_cast<char*>(ws);
   float* scores = page_scores ? page_scores : reinterpret_cast<float*>(wsb + w.scores);
-  PageScoreArgs pa;
   pa.pairs = reinterpret_cast<const float*>(wsb + w.delta);
   pa.rel_w = reinterpret_cast<const uint16_t*>(wsb + w.delta);
   pa.rel_max = reinterpret_cast<const float*>(wsb + w.rel_max);
-  pa.lse = reinterpret_cast<const float*>(wsb + w.lse);
   pa.seq_lens = c->d.seq_lens;
   pa.scores = scores;
   pa.t_pad = (int64_t)c->d.max_pages_per_seq * c->d.page_size;
@@ -621,9 +624,8 @@ lak_status lak_attn_delta_select(lak_cache* c, int32_t layer, const void* q, con
   pa.scope = scope;
   pa.tokens_per_block = kScoreTokensPerBlock;
   const int rows = scope == LAK_SCOPE_GROUP ? c->d.num_kv_heads : 1;
-  hipError_t e = (agg == LAK_AGG_SUM) ? launch_page_score_pairs(pa, c->batch, rows, c->max_np(), st)
-                                      : launch_page_score(pa, c->batch, rows, c->max_np(), st);
-  if (e != hipSuccess) return hip_fail(e, "page score launch");
+  hipError_t e = launch_delta_post(c->d.dtype, c->d.head_dim, pa, c->batch, rows, c->max_np(), st);
+  if (e != hipSuccess) return hip_fail(e, "delta post launch");
   return run_select(c, scores, scope, k_top, recency, sel, sel_count, sel_capacity, st);
 }
 

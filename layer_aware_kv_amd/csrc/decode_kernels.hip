@@ -19,6 +19,7 @@
 
 #include <algorithm>
 
+#include "lak_combine.h"
 #include "lak_device.h"
 #include "lak_internal.h"
 
@@ -616,79 +617,10 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
   }
 }
 
-// One wave per (head, sequence).  Lane s holds split s's weight; the weighted sum
-// over splits runs in split order with the weight broadcast from a scalar register
-// and all split loads of an unrolled group in flight together.
+// One wave per (head, sequence).
 template <int ESZ, int D>
 __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
-  constexpr int PER = D / 64;  // head-dim elements per lane
-  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int G = a.hq / a.hkv, g = h / G;
-  const int T = a.seq_lens[b];
-  int n_items;
-  if (a.sel_count) {
-    const int64_t row = (int64_t)b * a.sel_rows + (a.sel_rows == 1 ? 0 : g);
-    n_items = min(max(a.sel_count[row], 0), min(a.sel_cap, (T + a.page - 1) / a.page));
-  } else {
-    n_items = (T + a.page - 1) / a.page;
-  }
-  const int S = min((n_items + a.pps - 1) / a.pps, a.splits);
-  const int64_t row0 = ((int64_t)b * a.hq + h) * a.s_cap;
-  float M = -INFINITY;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, a.ml_part[(row0 + s) * 2]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
-  float acc[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float L = 0.f;
-  if (M != -INFINITY) {
-    for (int c0 = 0; c0 < S; c0 += 64) {
-      const int s_l = c0 + lane;
-      float wl = 0.f;
-      if (s_l < S) {
-        wl = exp2f(a.ml_part[(row0 + s_l) * 2] - M);
-        L += wl * a.ml_part[(row0 + s_l) * 2 + 1];
-      }
-      const int cn = min(64, S - c0);
-      const float* op = a.o_part + (row0 + c0) * D + lane * PER;
-      int s = 0;
-      for (; s + 8 <= cn; s += 8) {
-        float v[8][PER];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-          for (int e = 0; e < PER; ++e) v[u][e] = op[(int64_t)(s + u) * D + e];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s + u));
-#pragma unroll
-          for (int e = 0; e < PER; ++e) acc[e] += w * v[u][e];
-        }
-      }
-      for (; s < cn; ++s) {
-        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s));
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] += w * op[(int64_t)s * D + e];
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) L += shfl_xor_f(L, o);
-  }
-  const int64_t oi = ((int64_t)b * a.hq + h) * D + lane * PER;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const float val = (L > 0.f) ? acc[e] / L : 0.f;
-    if (ESZ == 2)
-      reinterpret_cast<uint16_t*>(a.out)[oi + e] = f32_to_bf16_rne(val);
-    else
-      reinterpret_cast<float*>(a.out)[oi + e] = val;
-  }
-  if (lane == 0) {
-    const float lse = (L > 0.f) ? (M + log2f(L)) * kLn2 : -INFINITY;
-    if (a.lse) a.lse[(int64_t)b * a.hq + h] = lse;
-    if (a.lse2) a.lse2[(int64_t)b * a.hq + h] = lse;
-  }
+  combine_head<ESZ, D>(a, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 template <int ESZ, int D, int U>

@@ -111,6 +111,24 @@ __device__ inline void encode_rows_fp8(int d, uint8_t* kb, uint8_t* vb, int tt, 
   }
 }
 
+// Statistics of one (row, head) over its S split partials ml[s] = (max in log2 units,
+// sum of 2^(logit - max)): M = max_s m_s and L = sum_s l_s 2^(m_s - M).  One whole wave;
+// lane s takes splits s, s + 64, ...; the fixed order gives every caller the same bits.
+__device__ inline void merge_split_stats(const float* ml, int S, int lane, float& M, float& L) {
+  float m = -INFINITY;
+  for (int s = lane; s < S; s += 64) m = fmaxf(m, ml[2 * s]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  float acc = 0.f;
+  if (m != -INFINITY) {
+    for (int s = lane; s < S; s += 64) acc += exp2f(ml[2 * s] - m) * ml[2 * s + 1];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  }
+  M = m;
+  L = acc;
+}
+
 // Inclusive prefix sum over a wave (64 lanes).
 __device__ inline int wave_incl_scan(int v, int lane) {
 #pragma unroll

@@ -51,14 +51,14 @@ struct CombineArgs {
   int splits;                 // splits launched by the decode kernel
   void* out;                  // [B][Hq][D]
   float* lse;                 // [B][Hq] (may be NULL)
-  float* lse2;                // second copy (may be NULL)
 };
 
 struct PageScoreArgs {
   const uint16_t* rel_w;      // MAX: relative weights and sub-tile maxima as the decode kernel
   const float* rel_max;       //      wrote them (DecodeArgs::rel_w, rel_max)
   const float* pairs;         // SUM: (max, sum) pairs
-  const float* lse;           // [B][Hq]
+  CombineArgs cb;             // the delta decode's split partials: each head's LSE is merged
+                              // from them, and extra blocks write the layer's out / lse
   const int32_t* seq_lens;
   float* scores;              // [B][R][max_pages]
   int64_t t_pad;
@@ -68,8 +68,10 @@ struct PageScoreArgs {
   int tokens_per_block;
 };
 
-// SUM aggregation from the decode kernel's (max, sum) pairs: no logits needed.
-hipError_t launch_page_score_pairs(const PageScoreArgs& a, int batch, int rows, int max_np, hipStream_t st);
+// Delta-layer post step in one launch: the split combine (out, lse) and the page scores
+// (MAX from the fp16 relative weights, SUM from the (max, sum) pairs).
+hipError_t launch_delta_post(int dtype, int D, const PageScoreArgs& a, int batch, int rows, int max_np,
+                             hipStream_t st);
 
 struct TopkArgs {
   const float* scores;        // [B][R][max_pages]
@@ -117,8 +119,6 @@ int tune_min_subtiles();
 hipError_t launch_decode(int dtype, int mode, int D, const DecodeArgs& a, int splits, int batch,
                          hipStream_t st);
 hipError_t launch_combine(int dtype, int D, const CombineArgs& a, int batch, hipStream_t st);
-hipError_t launch_page_score(const PageScoreArgs& a, int batch, int rows, int max_np,
-                             hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, int batch, hipStream_t st);
 hipError_t launch_step_update(const StepUpdate& u, int32_t* page_table, int32_t* seq_lens,
                               int max_pages, hipStream_t st);

@@ -1,37 +1,78 @@
 // Delta-layer page scoring and page selection ("Methodology in Plain English",
 // DELTA AI summary page): per token, the maximum (or sum) over the scope's heads of
 // the softmax weight exp(logit - lse); per page, the sum over its valid tokens;
-// then the last `recency` pages plus the `k_top` highest-scoring older pages.
+// then the last `recency` pages plus the `k_top` highest-scoring older pages.  The
+// scoring launch also combines the delta decode's split partials into the layer's
+// attention output.
 #include <math.h>
 
+#include "lak_combine.h"
 #include "lak_device.h"
 #include "lak_internal.h"
 
 namespace lak {
 
-// One block = `tokens_per_block` consecutive tokens of one score row; each thread
-// takes 4 consecutive tokens, so a page of P tokens is P/4 adjacent lanes and its
-// sum is a butterfly over them (fixed order: scores are bitwise reproducible).
-// Input: the decode kernel's blocks per (b, KV head g, 16-token sub-tile): [Gp heads]
-// [16 tokens] fp16 weights u relative to the head's sub-tile max r (log2 units), and
-// the maxima [Gp].  Token weight of head h: u * 2^(r - lse_h log2 e), the softmax
-// weight exp(logit - lse_h) up to the fp16 rounding of u.
-template <int P>
-__global__ __launch_bounds__(256) void page_score_kernel(PageScoreArgs a) {
+// Delta-layer post step, one launch.  Grid (n_chunks + combine blocks, score rows R,
+// batch).  Blocks x < n_chunks score pages of row (b, r); the others combine the split
+// partials of the row's heads (one head per wave: out and lse of the layer).  A scoring
+// block first merges, from the same partials and with the same routine as the combine
+// (merge_split_stats), the log-sum-exp of each head it aggregates.
+//
+// MAX (SUMP false): a block takes `tokens_per_block` consecutive tokens of its row, 4
+// per thread, so a page of P tokens is P/4 adjacent lanes and its sum is a butterfly
+// over them (fixed order: scores are bitwise reproducible).  Input: per (b, KV head g,
+// 16-token sub-tile) [Gp heads][16 tokens] fp16 weights u relative to the head's
+// sub-tile max r (log2 units) and the maxima [Gp]; token weight of head h:
+// u * 2^(r - lse2_h) = exp(logit - lse_h) up to the fp16 rounding of u.
+// SUM (SUMP true): one thread per page adds, over the scope's KV heads, the page's
+// sub-tiles and the group's heads, e * 2^(r - lse2_h) from the (r, e) pairs -- the sum
+// of exp(logit - lse_h) over the page's valid tokens.
+template <int P, int ESZ, int D, bool SUMP>
+__global__ __launch_bounds__(256) void delta_post_kernel(PageScoreArgs a, int n_chunks) {
   static_assert(P % 16 == 0 && P / 4 <= 64, "page of 16..256 tokens");
-  const int chunk = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
-  const int T = a.seq_lens[b];
-  const int NP = min((T + P - 1) / P, a.max_pages);
-  const int t_end = NP * P;
+  extern __shared__ float lse2_s[];  // log-sum-exp (log2 units) of the block's heads
+  const int r = blockIdx.y, b = blockIdx.z;
   const int G = a.hq / a.hkv;
-  const int Gp = G + (G & 1);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g_lo = a.scope == 0 ? r : 0;
   const int g_hi = a.scope == 0 ? r + 1 : a.hkv;
+  const int h_lo = g_lo * G, h_hi = g_hi * G;
+  if ((int)blockIdx.x >= n_chunks) {
+    const int h = h_lo + 4 * ((int)blockIdx.x - n_chunks) + wave;
+    if (h < h_hi) combine_head<ESZ, D>(a.cb, h, b, lane);
+    return;
+  }
+  for (int h = h_lo + wave; h < h_hi; h += 4) {
+    float M, L;
+    merge_split_stats(a.cb.ml_part + ((int64_t)b * a.hq + h) * a.cb.s_cap * 2, combine_splits(a.cb, b, h / G),
+                      lane, M, L);
+    if (lane == 0) lse2_s[h - h_lo] = (L > 0.f) ? M + log2f(L) : -INFINITY;
+  }
+  __syncthreads();
+  const int T = a.seq_lens[b];
+  const int NP = min((T + P - 1) / P, a.max_pages);
+  const int Gp = G + (G & 1);
   const int rows = a.scope == 0 ? a.hkv : 1;
   const int64_t nsub = a.t_pad / 16;
-  const float* ls = a.lse + (int64_t)b * a.hq;
   float* out = a.scores + ((int64_t)b * rows + r) * a.max_pages;
-  const int tb0 = chunk * a.tokens_per_block;
+  if (SUMP) {
+    const int jp = (int)blockIdx.x * blockDim.x + threadIdx.x;
+    if (jp >= NP) return;
+    const int spp = P / 16;
+    float acc = 0.f;
+    for (int g = g_lo; g < g_hi; ++g) {
+      for (int u = 0; u < spp; ++u) {
+        const int st = jp * spp + u;
+        if (st * 16 >= T) break;
+        const float* pp = a.pairs + ((((int64_t)b * a.hkv + g) * nsub + st) * Gp) * 2;
+        for (int h = 0; h < G; ++h) acc += pp[2 * h + 1] * exp2f(pp[2 * h] - lse2_s[g * G + h - h_lo]);
+      }
+    }
+    out[jp] = acc;
+    return;
+  }
+  const int t_end = NP * P;
+  const int tb0 = (int)blockIdx.x * a.tokens_per_block;
   const int tb1 = min(tb0 + a.tokens_per_block, t_end);
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   for (int base = tb0; base < tb1; base += 4 * blockDim.x) {
@@ -44,16 +85,13 @@ __global__ __launch_bounds__(256) void page_score_kernel(PageScoreArgs a) {
         const float* rp = a.rel_max + blk * Gp;
         for (int h = 0; h < G; ++h) {
           const u32x2 w = *reinterpret_cast<const u32x2*>(up + h * 16);
-          const float c = exp2f(rp[h] - ls[g * G + h] * kLog2e);
+          const float c = exp2f(rp[h] - lse2_s[g * G + h - h_lo]);
           const float u[4] = {(float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] & 0xFFFFu)),
                               (float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] >> 16)),
                               (float)__builtin_bit_cast(_Float16, (uint16_t)(w[1] & 0xFFFFu)),
                               (float)__builtin_bit_cast(_Float16, (uint16_t)(w[1] >> 16))};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = (t + e < T) ? u[e] * c : 0.f;
-            acc[e] = (a.agg == 0) ? fmaxf(acc[e], x) : acc[e] + x;
-          }
+          for (int e = 0; e < 4; ++e) acc[e] = fmaxf(acc[e], (t + e < T) ? u[e] * c : 0.f);
         }
       }
     }
@@ -64,55 +102,38 @@ __global__ __launch_bounds__(256) void page_score_kernel(PageScoreArgs a) {
   }
 }
 
-hipError_t launch_page_score(const PageScoreArgs& a, int batch, int rows, int max_np,
-                             hipStream_t st) {
-  if (batch == 0 || max_np == 0) return hipSuccess;
-  const int64_t tokens = (int64_t)max_np * a.page;
-  dim3 grid((unsigned)((tokens + a.tokens_per_block - 1) / a.tokens_per_block), rows, batch);
+template <int ESZ, int D, bool SUMP>
+static hipError_t launch_delta_post_t(const PageScoreArgs& a, int batch, int rows, int max_np, hipStream_t st) {
+  const int G = a.hq / a.hkv;
+  const int heads = (rows == 1) ? a.hq : G;  // heads per score row
+  const int n_chunks = SUMP ? (max_np + 255) / 256
+                            : (int)(((int64_t)max_np * a.page + a.tokens_per_block - 1) / a.tokens_per_block);
+  dim3 grid((unsigned)(n_chunks + (heads + 3) / 4), rows, batch);
+  const size_t lds = (size_t)heads * sizeof(float);
   switch (a.page) {
-    case 16: hipLaunchKernelGGL(page_score_kernel<16>, grid, dim3(256), 0, st, a); break;
-    case 32: hipLaunchKernelGGL(page_score_kernel<32>, grid, dim3(256), 0, st, a); break;
-    case 64: hipLaunchKernelGGL(page_score_kernel<64>, grid, dim3(256), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((delta_post_kernel<16, ESZ, D, SUMP>), grid, dim3(256), lds, st, a, n_chunks); break;
+    case 32: hipLaunchKernelGGL((delta_post_kernel<32, ESZ, D, SUMP>), grid, dim3(256), lds, st, a, n_chunks); break;
+    case 64: hipLaunchKernelGGL((delta_post_kernel<64, ESZ, D, SUMP>), grid, dim3(256), lds, st, a, n_chunks); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-// SUM aggregation without logits: one thread per page adds, over the scope's KV
-// heads, the page's sub-tiles and the group's heads, e * exp(r ln 2 - lse_h) from the
-// (r, e) pairs the delta decode kernel wrote per (b, g, sub-tile, head) -- that is
-// sum_t exp(logit_t - lse_h) over the page's valid tokens, exactly.
-__global__ __launch_bounds__(256) void page_score_pairs_kernel(PageScoreArgs a) {
-  const int r = blockIdx.y, b = blockIdx.z;
-  const int jp = blockIdx.x * blockDim.x + threadIdx.x;
-  const int T = a.seq_lens[b];
-  const int NP = min((T + a.page - 1) / a.page, a.max_pages);
-  if (jp >= NP) return;
-  const int G = a.hq / a.hkv;
-  const int Gp = G + (G & 1);
-  const int g_lo = a.scope == 0 ? r : 0;
-  const int g_hi = a.scope == 0 ? r + 1 : a.hkv;
-  const int rows = a.scope == 0 ? a.hkv : 1;
-  const int spp = a.page / 16;
-  const int64_t nsub = a.t_pad / 16;
-  const float* ls = a.lse + (int64_t)b * a.hq;
-  float acc = 0.f;
-  for (int g = g_lo; g < g_hi; ++g) {
-    for (int u = 0; u < spp; ++u) {
-      const int st = jp * spp + u;
-      if (st * 16 >= T) break;
-      const float* pp = a.pairs + ((((int64_t)b * a.hkv + g) * nsub + st) * Gp) * 2;
-      for (int h = 0; h < G; ++h) acc += pp[2 * h + 1] * expf(pp[2 * h] * kLn2 - ls[g * G + h]);
-    }
-  }
-  a.scores[((int64_t)b * rows + r) * a.max_pages + jp] = acc;
+template <int ESZ, int D>
+static hipError_t launch_delta_post_d(const PageScoreArgs& a, int batch, int rows, int max_np, hipStream_t st) {
+  return a.agg == 1 ? launch_delta_post_t<ESZ, D, true>(a, batch, rows, max_np, st)
+                    : launch_delta_post_t<ESZ, D, false>(a, batch, rows, max_np, st);
 }
 
-hipError_t launch_page_score_pairs(const PageScoreArgs& a, int batch, int rows, int max_np, hipStream_t st) {
-  if (batch == 0 || max_np == 0) return hipSuccess;
-  dim3 grid((unsigned)((max_np + 255) / 256), rows, batch);
-  hipLaunchKernelGGL(page_score_pairs_kernel, grid, dim3(256), 0, st, a);
-  return hipGetLastError();
+hipError_t launch_delta_post(int dtype, int D, const PageScoreArgs& a, int batch, int rows, int max_np,
+                             hipStream_t st) {
+  if (batch == 0) return hipSuccess;
+  const bool f32 = (dtype == 1);  // outputs: bfloat16 for bf16 and fp8 pools
+  if (D == 128) return f32 ? launch_delta_post_d<4, 128>(a, batch, rows, max_np, st)
+                           : launch_delta_post_d<2, 128>(a, batch, rows, max_np, st);
+  if (D == 64) return f32 ? launch_delta_post_d<4, 64>(a, batch, rows, max_np, st)
+                          : launch_delta_post_d<2, 64>(a, batch, rows, max_np, st);
+  return hipErrorInvalidValue;
 }
 
 // Order key of a score: float32 bits of a positive score (monotone for x >= 0);

@@ -145,9 +145,9 @@ def test_workspace_covers_logits_and_partials():
     st, h = _create(max_batch=4, max_pages=16, page=16, hq=8, hkv=2, d=64)
     ws = lib.lak_workspace_bytes(h)
     # delta scratch per (b, kv head, 16-token sub-tile, head of the group): 16 fp16 weights
-    # and one float maximum; plus the LSE copy [B][Hq]
+    # and one float maximum; plus the (max, sum) split partials [Hq][s_cap][2]
     blocks = 4 * 2 * 4 * (16 * 16 // 16)
-    assert ws >= blocks * (16 * 2 + 4) + 4 * 8 * 4
+    assert ws >= blocks * (16 * 2 + 4) + 8 * 2 * 4
     lib.lak_cache_destroy(h)
 
 
