@@ -330,3 +330,45 @@ def test_fidelity_recall_matches_oracle_mass():
         for h in range(case.q.shape[1]):
             toks = selected_tokens(sel[b, h // G, :int(cnt[b, h // G])].cpu().tolist(), T, P)
             assert abs(rec[b, h] - p[h, toks].sum()) < 5e-3
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f32", "fp8"])
+def test_fused_append_sparse_without_the_token_page(kv):
+    """A sparse call given k_new / v_new whose selection leaves out the page of this
+    step's token still appends it (split 0's store) and attends only to the selection."""
+    from layer_aware_kv_amd import PagedKVCache
+    from oracle import quant as Q
+    act = "bf16" if kv == "fp8" else kv
+    lens = [300, 129]
+    case = random_case(31, 2, 8, 2, 64, lens, act)
+    out, kg = {}, {}
+    for fused in (True, False):
+        cache = PagedKVCache(1, 2, 8, 2, 64, 16, 24, 48, kv)
+        cache.seq_reset([n - 1 for n in lens])
+        k, v = to_dev(case.K, act), to_dev(case.V, act)
+        cache.kv_prefill(0, k, v)
+        cache.step_begin()
+        kn = torch.stack([k[b, :, lens[b] - 1] for b in range(2)]).contiguous()
+        vn = torch.stack([v[b, :, lens[b] - 1] for b in range(2)]).contiguous()
+        q = to_dev(case.q, act)
+        sel = torch.tensor([[[0, 3, 5, -1], [1, 2, 7, -1]], [[0, 2, -1, -1], [4, 5, 6, -1]]], dtype=torch.int32,
+                           device="cuda")
+        cnt = torch.tensor([[3, 3], [2, 3]], dtype=torch.int32, device="cuda")
+        if fused:
+            o, _ = cache.attn_sparse(0, q, 0.125, sel, cnt, k_new=kn, v_new=vn)
+        else:
+            cache.kv_append(0, kn, vn)
+            o, _ = cache.attn_sparse(0, q, 0.125, sel, cnt)
+        torch.cuda.synchronize()
+        out[fused] = o.clone()
+        kg[fused] = [cache.kv_gather(0, b, g, lens[b] - 1, 1) for b in range(2) for g in range(2)]
+    assert torch.equal(out[True], out[False])
+    for (k1, v1), (k2, v2) in zip(kg[True], kg[False]):
+        assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    for b, T in enumerate(lens):
+        K, V = case.K[b, :, :T], case.V[b, :, :T]
+        if kv == "fp8":
+            K, V = Q.quantize_dequantize(K), Q.quantize_dequantize(V)
+        sels = [[j for j in sel[b, g, :int(cnt[b, g])].tolist()] for g in range(2)]
+        ref, _ = oracle.sparse_attention(case.q[b], K, V, sels, 16, 0.125)
+        assert_close(host(out[True][b]), ref, TOL["f32" if kv == "f32" else "bf16"], f"b={b}")
