@@ -186,6 +186,9 @@ def main():
                     help="heads aggregated per selection: each KV group, or all query heads")
     ap.add_argument("--delta-layers", default=None,
                     help="comma-separated delta-layer list replacing the workload's (sweeps)")
+    ap.add_argument("--salient-strength", type=float, default=None,
+                    help="salient keys = strength * direction + noise (workload default 4; the fidelity study's "
+                         "attention sharpness)")
     ap.add_argument("--kv-dtype", choices=["bf16", "fp8"], default=None,
                     help="KV pool element type (default: the workload's; fp8 = E4M3 codes + per-row scales)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -216,6 +219,9 @@ def main():
     if args.delta_layers is not None:
         import dataclasses
         wl = dataclasses.replace(wl, delta_layers=tuple(int(x) for x in args.delta_layers.split(",") if x != ""))
+    if args.salient_strength is not None:
+        import dataclasses
+        wl = dataclasses.replace(wl, salient_strength=args.salient_strength)
     W = wl.warmup if args.warmup is None else args.warmup
     K = wl.steps if args.steps is None else args.steps
     B, L, HQ, HKV, D, P = wl.batch, wl.num_layers, wl.hq, wl.hkv, wl.d, wl.page
@@ -320,6 +326,7 @@ def main():
             "page": P, "top_k_pages": wl.k_top, "recency_pages": wl.recency,
             "full_layers": list(wl.full_layers), "delta_layers": list(wl.delta_layers),
             "ragged_min": wl.ragged_min, "agg": args.agg, "scope": args.scope, "kv_dtype": kv_dtype,
+            "salient_strength": wl.salient_strength,
             "parallelism": "single GPU",
         },
         "roofline": {

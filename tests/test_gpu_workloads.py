@@ -12,14 +12,18 @@ from workload import philox as px
 pytestmark = pytest.mark.gpu
 
 
-def _dev(index):
+def _dev(index, strength=None):
+    import dataclasses
+    from workload import Recipe
     from workload.device import DeviceInputs
-    return DeviceInputs(recipe_for(index))
+    if strength is None:
+        return DeviceInputs(recipe_for(index))
+    return DeviceInputs(Recipe(dataclasses.replace(CONFIGS[index], salient_strength=strength)))
 
 
-@pytest.mark.parametrize("index", [0, 1, 4])
-def test_device_generator_equals_host(index):
-    d = _dev(index)
+@pytest.mark.parametrize("index,strength", [(0, None), (1, None), (4, None), (1, 6.3)])
+def test_device_generator_equals_host(index, strength):
+    d = _dev(index, strength)
     r, wl = d.r, d.wl
     T = min(wl.context, 3000)
     k = torch.empty((wl.batch, wl.hkv, T, wl.d), dtype=d.torch_dtype, device="cuda")

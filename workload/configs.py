@@ -32,6 +32,7 @@ class Workload:
     sm_scale: float
     q_mode: str                # "scaled_noise" | "salient"
     n_salient: int = 0
+    salient_strength: float = 4.0  # salient key = strength * direction + noise
     drift_every: int = 0       # steps between drift events (0: none)
     drift_frac: float = 0.0
     steps: int = 1             # timed decode steps

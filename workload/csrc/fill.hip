@@ -117,9 +117,10 @@ struct SalientArgs {
   int64_t stride_r, stride_t;
   uint32_t kind, layer;
   uint64_t seed;
+  float strength;
 };
 
-// Salient keys: out = f32(4 * dir) + f32(noise) at the listed positions.
+// Salient keys: out = f32(strength * dir) + f32(noise) at the listed positions.
 __global__ void apply_salient_kernel(SalientArgs a) {
   const int64_t ri = blockIdx.x;  // r * npos + i
   const int64_t r = ri / a.npos;
@@ -127,7 +128,7 @@ __global__ void apply_salient_kernel(SalientArgs a) {
   if (p < a.t_begin || p >= a.t_begin + a.t_count) return;
   for (int d = threadIdx.x; d < a.D; d += blockDim.x) {
     const float z32 = __double2float_rn(normal_at(a.seed, a.kind, a.layer, (uint32_t)r, (uint64_t)p * a.D + d));
-    const float v = __fadd_rn(4.0f * a.dirs[r * a.D + d], z32);
+    const float v = __fadd_rn(__fmul_rn(a.strength, a.dirs[r * a.D + d]), z32);
     store(a.out, a.dtype, r * a.stride_r + (p - a.t_begin) * a.stride_t + d, v);
   }
 }
@@ -142,6 +143,7 @@ struct RowsArgs {
   const int32_t* salient;
   uint32_t kind, layer;
   uint64_t seed;
+  float strength;
 };
 
 __global__ void fill_rows_kernel(RowsArgs a) {
@@ -151,7 +153,7 @@ __global__ void fill_rows_kernel(RowsArgs a) {
     const float z32 = __double2float_rn(
         normal_at(a.seed, a.kind, a.layer, (uint32_t)a.rows[i], (uint64_t)a.toks[i] * a.D + d));
     float v = z32;
-    if (a.dirs && a.salient && a.salient[i]) v = __fadd_rn(4.0f * a.dirs[(int64_t)i * a.D + d], z32);
+    if (a.dirs && a.salient && a.salient[i]) v = __fadd_rn(__fmul_rn(a.strength, a.dirs[(int64_t)i * a.D + d]), z32);
     store(a.out, a.dtype, (int64_t)i * a.D + d, v);
   }
 }
@@ -176,18 +178,18 @@ int wl_fill_tokens(void* out, int dtype, int64_t R, int64_t T, int D, const int3
 
 int wl_apply_salient(void* out, int dtype, int64_t R, int npos, int D, const int32_t* pos, const float* dirs,
                      int64_t t_begin, int64_t t_count, int64_t stride_r, int64_t stride_t, int kind, int layer,
-                     uint64_t seed, void* stream) {
+                     uint64_t seed, float strength, void* stream) {
   if (R <= 0 || npos <= 0) return 0;
   SalientArgs a{out, dtype, R, npos, D, pos, dirs, t_begin, t_count, stride_r, stride_t, (uint32_t)kind,
-                (uint32_t)layer, seed};
+                (uint32_t)layer, seed, strength};
   hipLaunchKernelGGL(apply_salient_kernel, dim3((unsigned)(R * npos)), dim3(128), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }
 
 int wl_fill_rows(void* out, int dtype, int n, int D, const int32_t* rows, const int32_t* toks, const float* dirs,
-                 const int32_t* salient, int kind, int layer, uint64_t seed, void* stream) {
+                 const int32_t* salient, int kind, int layer, uint64_t seed, float strength, void* stream) {
   if (n <= 0) return 0;
-  RowsArgs a{out, dtype, n, D, rows, toks, dirs, salient, (uint32_t)kind, (uint32_t)layer, seed};
+  RowsArgs a{out, dtype, n, D, rows, toks, dirs, salient, (uint32_t)kind, (uint32_t)layer, seed, strength};
   hipLaunchKernelGGL(fill_rows_kernel, dim3(n), dim3(128), 0, (hipStream_t)stream, a);
   return (int)hipGetLastError();
 }

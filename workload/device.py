@@ -24,8 +24,8 @@ def lib():
         L = C.CDLL(LIB_PATH)
         P, I, I64, U64, F = C.c_void_p, C.c_int, C.c_int64, C.c_uint64, C.c_float
         L.wl_fill_tokens.argtypes = [P, I, I64, I64, I, P, I64, I, I, U64, I64, I64, I, F, F, P, I, P]
-        L.wl_apply_salient.argtypes = [P, I, I64, I, I, P, P, I64, I64, I64, I64, I, I, U64, P]
-        L.wl_fill_rows.argtypes = [P, I, I, I, P, P, P, P, I, I, U64, P]
+        L.wl_apply_salient.argtypes = [P, I, I64, I, I, P, P, I64, I64, I64, I64, I, I, U64, C.c_float, P]
+        L.wl_fill_rows.argtypes = [P, I, I, I, P, P, P, P, I, I, U64, C.c_float, P]
         for f in (L.wl_fill_tokens, L.wl_apply_salient, L.wl_fill_rows):
             f.restype = I
         _lib = L
@@ -79,7 +79,8 @@ class DeviceInputs:
         if wl.n_salient:
             pos = self.salient_positions(epoch) if sal is None else sal
             _chk(lib().wl_apply_salient(_p(k_out), self.dt, R, wl.n_salient, wl.d, _p(pos), _p(self.dirs(layer)),
-                                        0, t_stride, t_stride * wl.d, wl.d, px.KIND_K, layer, self.r.seed, _st()),
+                                        0, t_stride, t_stride * wl.d, wl.d, px.KIND_K, layer, self.r.seed,
+                                        float(wl.salient_strength), _st()),
                  "wl_apply_salient")
 
     def fill_queries(self, layer, step0, n_steps, out):
@@ -123,5 +124,5 @@ class DeviceInputs:
         dirs = self.dirs(layer)[srow_t.long()].contiguous()
         k_rows = torch.empty((n, wl.d), dtype=self.torch_dtype, device=self.device)
         _chk(lib().wl_fill_rows(_p(k_rows), self.dt, n, wl.d, _p(srow_t), _p(toks_t), _p(dirs), _p(sal_t),
-                                px.KIND_K, layer, self.r.seed, _st()), "wl_fill_rows")
+                                px.KIND_K, layer, self.r.seed, float(wl.salient_strength), _st()), "wl_fill_rows")
         return rows_t, k_rows

@@ -6,7 +6,7 @@ position, step), drawn from ``philox.normals``; the device fill kernels in
 
 * prefilled length T0_b: ``context`` (or, ragged, ``ragged_min + w mod
   (context - ragged_min + 1)`` for the b-th raw word of the KIND_LEN stream);
-* K[l,b,g,t,:] = noise_K(t) (+ 4 w_{l,b,g} when t is a salient position of the
+* K[l,b,g,t,:] = noise_K(t) (+ s w_{l,b,g}, s = salient_strength (4 by default), when t is a salient position of the
   current drift epoch), V[l,b,g,t,:] = noise_V(t), rounded to the stored dtype;
   the token appended at decode step s sits at position T0_b + s and is plain noise;
 * salient direction w_{l,b,g} = n / |n| for n ~ N(0, I_D) (KIND_DIR), float32;
@@ -132,7 +132,7 @@ class Recipe:
         if sal:
             w = self.direction(layer, b, g)
             idx = np.asarray(sal) - t0
-            z32[idx] = (np.float32(4.0) * w)[None, :] + z32[idx]
+            z32[idx] = (np.float32(wl.salient_strength) * w)[None, :] + z32[idx]
         if wl.dtype == "bf16":
             z32 = px.bf16_round(z32)
         return z32.astype(np.float64)
