@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Decode-attention throughput of DELTA's three-tier layer stack on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload stack28_b16_t64k] [--no-cpu-baseline]
 
 Workload (default): the 28-layer attention-only decode stack at long reasoning
 length -- batch 16, context 65536 tokens, 28 query / 4 KV heads, head dim 128,
@@ -43,6 +43,7 @@ KERNEL_NAMES = {
     "sparse": "lak::decode_kernel<{esz}, 128, MODE_SPARSE>",
 }
 KV_ESZ = {"bf16": 2, "f32": 4, "fp8": 1}
+STACK_WORKLOADS = ["stack28_b8_t16k", "stack28_b16_t64k", "stack36_b32_t8k_32k"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -177,7 +178,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", type=int, default=3, choices=[2, 3, 4])
+    ap.add_argument("--workload", default="stack28_b16_t64k", choices=STACK_WORKLOADS,
+                    help="layer-stack workload (default: batch 16 at context 65536)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1, help="batch rows in the CPU oracle sample")
     ap.add_argument("--agg", choices=["max", "sum"], default="max",
@@ -206,16 +208,17 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(--gpus must be 1; see DESIGN.md for how the path would shard).", file=sys.stderr)
+        print("bench.py runs on one GPU only (--gpus must be 1): sequences and, with per-group "
+              "selection, KV heads are independent, so the path would shard by batch or KV head with no "
+              "exchange; it is measured here on one GPU's share.", file=sys.stderr)
         sys.exit(2)
 
     import torch
     from layer_aware_kv_amd import accounting as acc
     from layer_aware_kv_amd._lib import event_elapsed_ms
-    from workload import CONFIGS
+    from workload import get
 
-    wl = CONFIGS[args.config]
+    wl = get(args.workload)
     if args.delta_layers is not None:
         import dataclasses
         wl = dataclasses.replace(wl, delta_layers=tuple(int(x) for x in args.delta_layers.split(",") if x != ""))

@@ -9,25 +9,26 @@ import torch
 
 import oracle
 from tests.gpu_util import TOL, LSE_TOL, assert_close, check_selection
-from workload import CONFIGS
+from workload import WORKLOADS
 
 pytestmark = pytest.mark.gpu
 
 SAMPLES = {
     # workload: timed/warm-up steps, steps checked, batch rows, layers checked
-    2: dict(warmup=0, steps=256, check=[0, 100, 255], rows=[0, 7], layers=[0, 2, 3, 23, 27]),
-    3: dict(warmup=4, steps=2, check=[4], rows=[0, 15], layers=[0, 2, 3, 23, 27]),
-    4: dict(warmup=4, steps=2, check=[5], rows=None, layers=[0, 2, 3, 34, 35]),
+    "stack28_b8_t16k": dict(warmup=0, steps=256, check=[0, 100, 255], rows=[0, 7], layers=[0, 2, 3, 23, 27]),
+    "stack28_b16_t64k": dict(warmup=4, steps=2, check=[4], rows=[0, 15], layers=[0, 2, 3, 23, 27]),
+    "stack36_b32_t8k_32k": dict(warmup=4, steps=2, check=[5], rows=None, layers=[0, 2, 3, 34, 35]),
 }
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("index,kv", [(2, None), (3, None), (4, None), (3, "fp8")])
-def test_stack_full_size_sampled(index, kv):
+@pytest.mark.parametrize("name,kv", [("stack28_b8_t16k", None), ("stack28_b16_t64k", None),
+                                     ("stack36_b32_t8k_32k", None), ("stack28_b16_t64k", "fp8")])
+def test_stack_full_size_sampled(name, kv):
     import bench
     from oracle.quant import quantize_dequantize
-    wl = CONFIGS[index]
-    spec = SAMPLES[index]
+    wl = WORKLOADS[name]
+    spec = SAMPLES[name]
     print(f"stack parity: {wl.name} kv {kv or wl.dtype}", flush=True)
     sb = bench.StackBench(wl, spec["warmup"], spec["steps"], kv_dtype=kv)
     rec, tiers, lens0 = sb.rec, sb.tiers, sb.lens0

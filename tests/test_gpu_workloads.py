@@ -6,24 +6,25 @@ import torch
 
 import oracle
 from tests.gpu_util import TOL, LSE_TOL, assert_close, check_selection, host
-from workload import recipe_for, CONFIGS
+from workload import recipe_for, WORKLOADS
 from workload import philox as px
 
 pytestmark = pytest.mark.gpu
 
 
-def _dev(index, strength=None):
+def _dev(name, strength=None):
     import dataclasses
     from workload import Recipe
     from workload.device import DeviceInputs
     if strength is None:
-        return DeviceInputs(recipe_for(index))
-    return DeviceInputs(Recipe(dataclasses.replace(CONFIGS[index], salient_strength=strength)))
+        return DeviceInputs(recipe_for(name))
+    return DeviceInputs(Recipe(dataclasses.replace(WORKLOADS[name], salient_strength=strength)))
 
 
-@pytest.mark.parametrize("index,strength", [(0, None), (1, None), (4, None), (1, 6.3)])
-def test_device_generator_equals_host(index, strength):
-    d = _dev(index, strength)
+@pytest.mark.parametrize("name,strength", [("layer1_f32_b1_t1k", None), ("layer1_bf16_b1_t8k", None),
+                                           ("stack36_b32_t8k_32k", None), ("layer1_bf16_b1_t8k", 6.3)])
+def test_device_generator_equals_host(name, strength):
+    d = _dev(name, strength)
     r, wl = d.r, d.wl
     T = min(wl.context, 3000)
     k = torch.empty((wl.batch, wl.hkv, T, wl.d), dtype=d.torch_dtype, device="cuda")
@@ -48,10 +49,10 @@ def test_device_generator_equals_host(index, strength):
             assert np.array_equal(host(q[s, b]), r.q(0, 5 + s, b))
 
 
-def _run_single_layer(index):
-    """Workloads 0 and 1: one layer run as full, delta-select and sparse."""
+def _run_single_layer(name):
+    """The single-layer workloads: one layer run as full, delta-select and sparse."""
     from layer_aware_kv_amd import PagedKVCache
-    d = _dev(index)
+    d = _dev(name)
     r, wl = d.r, d.wl
     T = wl.context
     cache = PagedKVCache(1, wl.batch, wl.hq, wl.hkv, wl.d, wl.page, wl.max_pages_per_seq() + 1,
@@ -68,12 +69,13 @@ def _run_single_layer(index):
     return d, cache, q[0]
 
 
-@pytest.mark.parametrize("index", [0, 1])
-def test_single_layer_workload_full_delta_sparse(index):
-    d, cache, q = _run_single_layer(index)
+@pytest.mark.parametrize("name", ["layer1_f32_b1_t1k", "layer1_bf16_b1_t8k"])
+def test_single_layer_workload_full_delta_sparse(name):
+    d, cache, q = _run_single_layer(name)
     r, wl = d.r, d.wl
     T = wl.context
-    aggs = ["max", "sum"] if index == 0 else ["max"]
+    salient = wl.q_mode == "salient"
+    aggs = ["max"] if salient else ["max", "sum"]
     for agg in aggs:
         scores = torch.zeros((wl.batch, wl.hkv, cache.max_pages), device="cuda")
         out_f, lse_f = cache.attn_full(0, q, wl.sm_scale)
@@ -98,7 +100,7 @@ def test_single_layer_workload_full_delta_sparse(index):
         ref_s, ref_ls = oracle.sparse_attention(qh, K, V, sels, wl.page, wl.sm_scale)
         assert_close(host(out_s[0]), ref_s, TOL[wl.dtype], "sparse")
         assert_close(host(lse_s[0]), ref_ls, LSE_TOL[wl.dtype], "sparse lse")
-        if index == 1:
+        if salient:
             # the salient far keys are in the selection of every group
             for g in range(wl.hkv):
                 sal_pages = {p // wl.page for p in r.salient_slots(0, g, 0)}

@@ -4,7 +4,7 @@ import pytest
 import torch
 
 from workload import philox as px
-from workload import recipe_for, CONFIGS
+from workload import recipe_for, WORKLOADS as W
 
 
 def _hex(words):
@@ -45,8 +45,8 @@ def test_bf16_rounding_matches_torch():
     assert np.array_equal(ours, ref)
 
 
-def test_recipe_structure_cfg1():
-    r = recipe_for(1)
+def test_recipe_structure_single_layer_8k():
+    r = recipe_for("layer1_bf16_b1_t8k")
     wl = r.wl
     T = wl.context
     sal = r.salient_slots(0, 1, 0)
@@ -66,7 +66,7 @@ def test_recipe_structure_cfg1():
 
 
 def test_recipe_drift_moves_ten_percent():
-    r = recipe_for(2)
+    r = recipe_for("stack28_b8_t16k")
     moves = r.drift_moves(1)
     wl = r.wl
     assert len(moves) == wl.batch * wl.hkv * wl.drift_count
@@ -75,8 +75,8 @@ def test_recipe_drift_moves_ten_percent():
         assert new < wl.context + wl.drift_every - wl.recency * wl.page
 
 
-def test_ragged_lengths_cfg4():
-    r = recipe_for(4)
+def test_ragged_lengths_stack36():
+    r = recipe_for("stack36_b32_t8k_32k")
     L = r.lengths0()
     assert L.shape == (32,) and L.min() >= 8192 and L.max() <= 32768
     assert len(set(L.tolist())) > 16
@@ -84,8 +84,10 @@ def test_ragged_lengths_cfg4():
 
 def test_config_budgets_match_workload_text():
     # configs 1-4 state budgets in tokens "incl. recency"; top-k = (budget - recency) / P
-    assert CONFIGS[1].k_top * 16 == 1536 and CONFIGS[1].recency * 16 == 512
-    assert (CONFIGS[2].k_top + CONFIGS[2].recency) * 16 == 2048
-    assert (CONFIGS[3].k_top + CONFIGS[3].recency) * 16 == 4096 and CONFIGS[3].recency * 16 == 1024
-    assert (CONFIGS[4].k_top + CONFIGS[4].recency) * 32 == 4096 and CONFIGS[4].recency * 32 == 1024
-    assert CONFIGS[0].k_top == 8 and CONFIGS[0].recency * 16 == 64
+    a, b, c, d, e = (W[n] for n in ("layer1_f32_b1_t1k", "layer1_bf16_b1_t8k", "stack28_b8_t16k",
+                                     "stack28_b16_t64k", "stack36_b32_t8k_32k"))
+    assert b.k_top * 16 == 1536 and b.recency * 16 == 512
+    assert (c.k_top + c.recency) * 16 == 2048
+    assert (d.k_top + d.recency) * 16 == 4096 and d.recency * 16 == 1024
+    assert (e.k_top + e.recency) * 32 == 4096 and e.recency * 32 == 1024
+    assert a.k_top == 8 and a.recency * 16 == 64

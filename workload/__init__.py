@@ -4,5 +4,5 @@ Shared by the oracle side (host, ``recipe``) and the device side (``device``,
 fill kernels in ``csrc/fill.hip``).  It draws numbers only; it holds none of the
 attention method's arithmetic.
 """
-from .configs import CONFIGS, Workload, get  # noqa: F401
+from .configs import STACKS, WORKLOADS, Workload, get  # noqa: F401
 from .recipe import Recipe, recipe_for  # noqa: F401

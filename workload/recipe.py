@@ -168,6 +168,6 @@ class Recipe:
 
 
 @lru_cache(maxsize=8)
-def recipe_for(index: int) -> Recipe:
+def recipe_for(name: str) -> Recipe:
     from .configs import get
-    return Recipe(get(index))
+    return Recipe(get(name))
