@@ -132,8 +132,10 @@ lak_status lak_page_table_host(const lak_cache* cache, int32_t b, int32_t* out, 
 int64_t lak_free_pages(const lak_cache* cache);
 
 /* Workspace for the attention calls of this cache at its capacity (max_batch,
- * max_pages_per_seq): split-K partials, combine LSE, delta-layer logits and
- * page-score scratch.  Device memory, any contents, 256-byte aligned. */
+ * max_pages_per_seq): split-K partials, the delta-layer scratch (per head and
+ * 16-token sub-tile, the maximum logit and fp16 weights relative to it, or the
+ * (max, sum) pairs for SUM) and page-score scratch.  Device memory, any contents,
+ * 256-byte aligned; calls read nothing a previous call left in it. */
 size_t lak_workspace_bytes(const lak_cache* cache);
 
 /* Writes this step's key and value of every active sequence into layer `layer` at
@@ -187,7 +189,9 @@ lak_status lak_attn_full(lak_cache* cache, int32_t layer, const void* q, const v
  * sel[row][0 .. count), -1 after; sel_count[row] = count = min(NP_b, k_top + recency).
  * sel: device int32 [B][R][sel_capacity], R = Hkv (GROUP) or 1 (ALL),
  * sel_capacity >= k_top + recency.  page_scores (nullable): device float32
- * [B][R][max_pages_per_seq], entries j >= NP_b left untouched. */
+ * [B][R][max_pages_per_seq], entries j >= NP_b left untouched; MAX scores come from
+ * fp16 weights relative to each head's 16-token maximum (relative error <= 2^-11),
+ * SUM scores are exact up to float32 rounding. */
 lak_status lak_attn_delta_select(lak_cache* cache, int32_t layer, const void* q, const void* k_new,
                                  const void* v_new, float sm_scale, void* out, float* lse,
                                  int32_t k_top, int32_t recency,
