@@ -174,3 +174,23 @@ def test_tier_bytes_and_selected_tokens():
     assert sp == 2048 * 4 * 128 * 2 * 2 + 2 * 28 * 128 * 2 + 4 * 128 * 4
     tiers = ["full", "full", "delta"] + ["sparse"] * 3
     assert acc.attended_tokens([4096], tiers, 16, 64, 8) == 3 * 4096 + 3 * 72 * 16
+
+
+def test_header_is_plain_c():
+    """include/lak.h compiles as C99 (no C++ or HIP types in the ABI) and a C caller
+    can name every entry point."""
+    import shutil
+    import subprocess
+    import tempfile
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    calls = "\n".join(f"  (void)&{n};" for n in _declared_symbols())
+    src = f'#include "lak.h"\nint main(void) {{\n{calls}\n  return 0;\n}}\n'
+    with tempfile.TemporaryDirectory() as d:
+        path = os.path.join(d, "use_lak.c")
+        with open(path, "w") as f:
+            f.write(src)
+        r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                            "-I", os.path.join(ROOT, "include"), path], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
