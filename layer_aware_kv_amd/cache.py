@@ -31,8 +31,10 @@ def _stream():
 class PagedKVCache:
     """One paged GQA KV cache shared by all layers (one K and one V pool per layer).
 
-    Pools hold ``num_pages`` pages of [Hkv][P][D] elements each; the page table and
-    sequence lengths live in device memory and are maintained by the library.
+    Pools hold ``num_pages`` pages of [Hkv][P][D] elements each (``dtype`` "bf16",
+    "f32", or "fp8": E4M3 codes plus a float32 scale per token row); the page table and
+    sequence lengths live in device memory and are maintained by the library.  q, out,
+    k_new / v_new and prefill rows use ``torch_dtype`` (bfloat16 for an fp8 cache).
     """
 
     def __init__(self, num_layers, max_batch, num_q_heads, num_kv_heads, head_dim, page_size,
@@ -118,7 +120,8 @@ class PagedKVCache:
         L.check(L.lib().lak_kv_append(self._h, layer, _ptr(k_new), _ptr(v_new), _stream()), "lak_kv_append")
 
     def kv_prefill(self, layer, k, v):
-        """k, v: [B][Hkv][t_stride][D] contiguous."""
+        """k, v: [B][Hkv][t_stride][D] contiguous, in the activation dtype (bfloat16 rows are
+        encoded for an fp8 cache)."""
         L.check(L.lib().lak_kv_prefill(self._h, layer, _ptr(k), _ptr(v), k.shape[2], _stream()), "lak_kv_prefill")
 
     def kv_write_rows(self, layer, rows, k_rows, v_rows=None):

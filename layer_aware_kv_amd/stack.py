@@ -86,7 +86,8 @@ class DeltaStack:
         return d
 
     def step(self, q, k_new, v_new, tracer=None):
-        """One decode step.  q [L][B][Hq][D]; k_new, v_new [L][B][Hkv][D] (cache dtype).
+        """One decode step.  q [L][B][Hq][D]; k_new, v_new [L][B][Hkv][D] (the cache's activation
+        dtype: bfloat16 for bf16 and fp8 pools, float32 for f32 pools).
 
         ``tracer`` (optional) has ``pair(layer, tier)`` returning a (before, after)
         torch.cuda.Event pair to record around that layer's decode kernel, or None.
