@@ -458,8 +458,7 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
       s2[r] = (tb + r < T) ? sacc[r] * qk_scale2 : -INFINITY;
       mx = fmaxf(mx, s2[r]);
     }
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    mx = xor32_max(xor16_max(mx));
     const float m_new = fmaxf(m2, mx);
     const float alpha = exp2f(m2 - m_new);
     float p[4];
@@ -484,8 +483,7 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
 #pragma unroll
         for (int r = 0; r < 4; ++r) e += exp2f(s2[r] - mx);
       }
-      e += shfl_xor_f(e, 16);
-      e += shfl_xor_f(e, 32);
+      e = xor32_add(xor16_add(e));
       if (head_ok && j == 0) {
         const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + ct / kSub;
         typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -575,8 +573,7 @@ __global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_k
     __syncthreads();  // the merge below reuses this LDS
   }
 
-  l += shfl_xor_f(l, 16);
-  l += shfl_xor_f(l, 32);
+  l = xor32_add(xor16_add(l));
 
   // merge the waves of this workgroup through LDS
   float* lo = lds;                       // [kWaves][G][D]

@@ -52,6 +52,27 @@ __device__ inline int64_t subtile_base(int64_t phys, int g, int t_in_page, int h
 // Wave-level helpers
 // ---------------------------------------------------------------------------
 __device__ inline float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// Pairwise combine with the lane 16 (or 32) apart, in registers: v_permlane16_swap /
+// v_permlane32_swap (gfx950) leave lane l holding {v_l, v_(l^16)} (or ^32) across
+// their two results, so no LDS crossbar round trip is needed.  Max and add are
+// commutative, so the result equals v op shfl_xor(v, 16 or 32) bit for bit.
+__device__ inline float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor16_add(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float xor32_add(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 __device__ inline int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
 
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
