@@ -372,3 +372,34 @@ def test_fused_append_sparse_without_the_token_page(kv):
         sels = [[j for j in sel[b, g, :int(cnt[b, g])].tolist()] for g in range(2)]
         ref, _ = oracle.sparse_attention(case.q[b], K, V, sels, 16, 0.125)
         assert_close(host(out[True][b]), ref, TOL["f32" if kv == "f32" else "bf16"], f"b={b}")
+
+
+def test_attention_calls_replay_in_a_graph():
+    """The attention entry points launch kernels only (no memset, no host wait), so a
+    captured full / delta-select / sparse sequence replays exactly: every replay,
+    separated by eager work and synchronisation, equals the eager result."""
+    case, P, sm = _case(CASES[2])
+    cache = make_cache(case, P)
+    q = fill_and_step(cache, case)
+    out_f, lse_f = cache.attn_full(0, q, sm)
+    out_d, lse_d, sel, cnt = cache.attn_delta_select(0, q, sm, 20, 3)
+    out_s, lse_s = cache.attn_sparse(0, q, sm, sel, cnt)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out_f, lse_f, out_d, lse_d, sel, cnt, out_s, lse_s)]
+    bufs = [torch.empty_like(t) for t in ref]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=side):
+        cache.attn_full(0, q, sm, bufs[0], bufs[1])
+        cache.attn_delta_select(0, q, sm, 20, 3, out=bufs[2], lse=bufs[3], sel=bufs[4], sel_count=bufs[5])
+        cache.attn_sparse(0, q, sm, bufs[4], bufs[5], out=bufs[6], lse=bufs[7])
+    for rep in range(3):
+        for b in bufs:
+            b.zero_()
+        cache.attn_full(0, q, 0.5 * sm)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, exp in zip(bufs, ref):
+            assert torch.equal(got, exp), f"replay {rep}"
