@@ -94,14 +94,17 @@ struct Frag<2, D> {
       for (int i = 0; i < NL; ++i) k[i] = *reinterpret_cast<const u32x4*>(kr + (4 * i + j) * 8);
     }
     if (j == tt / 4) {
-      const int e = tt & 3;
 #pragma unroll
       for (int i = 0; i < NL; ++i)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const uint32_t val = vr[16 * (2 * i + h) + n];
-          const int x = h * 4 + e, sh = 16 * (x & 1);
-          v[i][x >> 1] = (v[i][x >> 1] & ~(0xFFFFu << sh)) | (val << sh);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)  // compile-time element index
+            if (e == (tt & 3)) {
+              const int x = h * 4 + e, sh = 16 * (x & 1);
+              v[i][x >> 1] = (v[i][x >> 1] & ~(0xFFFFu << sh)) | (val << sh);
+            }
         }
     }
   }
@@ -172,7 +175,10 @@ struct Frag<4, D> {
     }
     if (j == tt / 4) {
 #pragma unroll
-      for (int i = 0; i < NL; ++i) v[i][tt & 3] = vr[16 * i + n];
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)  // compile-time element index (a runtime one goes to scratch)
+          if (e == (tt & 3)) v[i][e] = vr[16 * i + n];
     }
   }
   __device__ inline void pv(f32x4* o, const float* p) const {
@@ -279,9 +285,11 @@ struct ElemT<2> { typedef uint16_t T; };
 template <>
 struct ElemT<4> { typedef uint32_t T; };
 
-// At least 4 waves per SIMD for the single-sub-tile batch (register budget 128).
+// At least 4 waves per SIMD for the single-sub-tile batch (register budget 128); fp32
+// fragments (q, K, V and the output accumulator at 32 registers each for D = 128) take the
+// 3-wave budget instead of spilling.
 template <int ESZ, int D, int MODE, int U>
-__global__ __launch_bounds__(256, (U == 1 ? 4 : (U == 2 ? 3 : 2))) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) void decode_kernel(DecodeArgs a) {
   typedef typename ElemT<ESZ>::T E;
   typedef typename ElemT<ESZ == 1 ? 2 : ESZ>::T QE;  // q rows: bfloat16 for fp8 pools
   typedef Frag<ESZ, D> F;
@@ -638,13 +646,20 @@ static hipError_t launch_decode_t(int mode, const DecodeArgs& a, int splits, int
   if (mode == MODE_DELTA && a.lds_stage && !a.sum_pairs)
     lds = std::max(lds, delta_stage_bytes(a.pps, a.page, G));
   dim3 grid(splits, a.hkv, batch);
-  const int u = tune_decode_batch(mode);
-  if (u == 4)
-    launch_decode_u<ESZ, D, 4>(mode, a, grid, lds, st);
-  else if (u == 2)
-    launch_decode_u<ESZ, D, 2>(mode, a, grid, lds, st);
-  else
-    launch_decode_u<ESZ, D, 1>(mode, a, grid, lds, st);
+  // fp32 pools always load one sub-tile at a time: their fragments fill the register
+  // budget of a deeper batch.
+  const int u = ESZ == 4 ? 1 : tune_decode_batch(mode);
+  if constexpr (ESZ != 4) {
+    if (u == 4) {
+      launch_decode_u<ESZ, D, 4>(mode, a, grid, lds, st);
+      return hipGetLastError();
+    }
+    if (u == 2) {
+      launch_decode_u<ESZ, D, 2>(mode, a, grid, lds, st);
+      return hipGetLastError();
+    }
+  }
+  launch_decode_u<ESZ, D, 1>(mode, a, grid, lds, st);
   return hipGetLastError();
 }
 
