@@ -25,14 +25,10 @@
 
 namespace lak {
 
-// 16-byte fragment load.  STREAM marks it non-temporal: the K/V stream of a full
-// pass (gigabytes) then does not evict from the caches what is reused soon (the
-// delta-layer scratch, the page table, the partials).
-template <bool STREAM>
-__device__ inline u32x4 load16(const u32x4* p) {
-  if (STREAM) return __builtin_nontemporal_load(p);
-  return *p;
-}
+// 16-byte fragment load, non-temporal: K/V pages are read once per call, so they do
+// not evict from the caches what is reused soon (the delta-layer scratch, the page
+// table, the selection, the partials).
+__device__ inline u32x4 load16(const u32x4* p) { return __builtin_nontemporal_load(p); }
 
 template <int ESZ, int D>
 struct Frag;
@@ -47,14 +43,13 @@ struct Frag<2, D> {
   u32x4 k[NL], v[NL];
   typedef bf16x8 QF;
 
-  template <bool STREAM>
   __device__ inline void load(const uint16_t* kb, const uint16_t* vb, const float*, const float*, int lane) {
     const u32x4* kp = reinterpret_cast<const u32x4*>(kb);
     const u32x4* vp = reinterpret_cast<const u32x4*>(vb);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) k[i] = load16<STREAM>(kp + i * 64 + lane);
+    for (int i = 0; i < NL; ++i) k[i] = load16(kp + i * 64 + lane);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) v[i] = load16<STREAM>(vp + i * 64 + lane);
+    for (int i = 0; i < NL; ++i) v[i] = load16(vp + i * 64 + lane);
   }
   // lane l: head l%16, head-dim chunk (4i + l/16)*8 .. +8
   __device__ static inline void load_q(QF* qf, const uint16_t* qrow, bool valid, int j) {
@@ -132,14 +127,13 @@ struct Frag<4, D> {
   u32x4 k[NL], v[NL];
   typedef f32x4 QF;
 
-  template <bool STREAM>
   __device__ inline void load(const uint32_t* kb, const uint32_t* vb, const float*, const float*, int lane) {
     const u32x4* kp = reinterpret_cast<const u32x4*>(kb);
     const u32x4* vp = reinterpret_cast<const u32x4*>(vb);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) k[i] = load16<STREAM>(kp + i * 64 + lane);
+    for (int i = 0; i < NL; ++i) k[i] = load16(kp + i * 64 + lane);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) v[i] = load16<STREAM>(vp + i * 64 + lane);
+    for (int i = 0; i < NL; ++i) v[i] = load16(vp + i * 64 + lane);
   }
   // lane l: head l%16, head-dim elements 16i + 4(l/16) .. +4
   __device__ static inline void load_q(QF* qf, const uint32_t* qrow, bool valid, int j) {
@@ -203,17 +197,16 @@ struct Frag<1, D> {
   u32x4 ks, vs;  // float bits of the key / value scales of tokens 4(l/16) .. +4
   typedef bf16x8 QF;
 
-  template <bool STREAM>
   __device__ inline void load(const uint8_t* kb, const uint8_t* vb, const float* ksb, const float* vsb,
                               int lane) {
     const u32x4* kp = reinterpret_cast<const u32x4*>(kb);
     const u32x4* vp = reinterpret_cast<const u32x4*>(vb);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) k[i] = load16<STREAM>(kp + i * 64 + lane);
+    for (int i = 0; i < NL; ++i) k[i] = load16(kp + i * 64 + lane);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) v[i] = load16<STREAM>(vp + i * 64 + lane);
-    ks = load16<STREAM>(reinterpret_cast<const u32x4*>(ksb) + (lane >> 4));
-    vs = load16<STREAM>(reinterpret_cast<const u32x4*>(vsb) + (lane >> 4));
+    for (int i = 0; i < NL; ++i) v[i] = load16(vp + i * 64 + lane);
+    ks = load16(reinterpret_cast<const u32x4*>(ksb) + (lane >> 4));
+    vs = load16(reinterpret_cast<const u32x4*>(vsb) + (lane >> 4));
   }
   // Lane l of load i holds token l%16, head-dim elements 16(4i + l/16) .. +16; the
   // first 8 feed MFMA 2i, the other 8 MFMA 2i+1, so q operand m of lane l holds
@@ -439,8 +432,7 @@ __global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) v
     const bool valid = lp >= 0 && t0 < T;
     const int64_t phys = item_pid(k);
     const int64_t row0 = valid ? (phys * a.hkv + g) * P + sub * kSub : 0;  // first token row
-    f.template load<MODE != MODE_SPARSE>(kpool + row0 * D, vpool + row0 * D, a.k_scale + row0,
-                                         a.v_scale + row0, lane);
+    f.load(kpool + row0 * D, vpool + row0 * D, a.k_scale + row0, a.v_scale + row0, lane);
     return Sub{valid, t0};
   };
 
@@ -622,10 +614,10 @@ __global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) v
   }
 }
 
-// One wave per (head, sequence).
-template <int ESZ, int D>
+// One wave per (head, sequence); NF: splits loaded in one round (0: the looped path).
+template <int ESZ, int D, int NF>
 __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
-  combine_head<ESZ, D>(a, blockIdx.x, blockIdx.y, threadIdx.x);
+  combine_head<ESZ, D, NF>(a, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 template <int ESZ, int D, int U>
@@ -679,14 +671,26 @@ hipError_t launch_decode(int dtype, int mode, int D, const DecodeArgs& a, int sp
   return hipErrorInvalidValue;
 }
 
+template <int ESZ, int D>
+static void launch_combine_t(const CombineArgs& a, dim3 grid, hipStream_t st) {
+  if (a.s_cap >= 1 && a.s_cap <= 8)
+    hipLaunchKernelGGL((combine_kernel<ESZ, D, 8>), grid, dim3(64), 0, st, a);
+  else if (a.s_cap >= 1 && a.s_cap <= 16)
+    hipLaunchKernelGGL((combine_kernel<ESZ, D, 16>), grid, dim3(64), 0, st, a);
+  else if (a.s_cap >= 1 && a.s_cap <= 32)
+    hipLaunchKernelGGL((combine_kernel<ESZ, D, 32>), grid, dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<ESZ, D, 0>), grid, dim3(64), 0, st, a);
+}
+
 hipError_t launch_combine(int dtype, int D, const CombineArgs& a, int batch, hipStream_t st) {
   if (batch == 0) return hipSuccess;
   dim3 grid(a.hq, batch);
   if (dtype == 2) dtype = 0;  // fp8 pools: bfloat16 outputs
-  if (dtype == 0 && D == 128) hipLaunchKernelGGL((combine_kernel<2, 128>), grid, dim3(64), 0, st, a);
-  else if (dtype == 0 && D == 64) hipLaunchKernelGGL((combine_kernel<2, 64>), grid, dim3(64), 0, st, a);
-  else if (dtype == 1 && D == 128) hipLaunchKernelGGL((combine_kernel<4, 128>), grid, dim3(64), 0, st, a);
-  else if (dtype == 1 && D == 64) hipLaunchKernelGGL((combine_kernel<4, 64>), grid, dim3(64), 0, st, a);
+  if (dtype == 0 && D == 128) launch_combine_t<2, 128>(a, grid, st);
+  else if (dtype == 0 && D == 64) launch_combine_t<2, 64>(a, grid, st);
+  else if (dtype == 1 && D == 128) launch_combine_t<4, 128>(a, grid, st);
+  else if (dtype == 1 && D == 64) launch_combine_t<4, 64>(a, grid, st);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

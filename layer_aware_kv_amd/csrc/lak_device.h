@@ -150,6 +150,22 @@ __device__ inline void merge_split_stats(const float* ml, int S, int lane, float
   L = acc;
 }
 
+// The same statistics when each lane holds at most one split: (m, l) of split `lane`,
+// m = -inf on lanes without one.  For S <= 64 this is bitwise merge_split_stats.
+__device__ inline void merge_lane_stats(float m_lane, float l_lane, float& M, float& L) {
+  float m = m_lane;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  float acc = 0.f;
+  if (m != -INFINITY) {
+    if (m_lane != -INFINITY) acc += exp2f(m_lane - m) * l_lane;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  }
+  M = m;
+  L = acc;
+}
+
 // Inclusive prefix sum over a wave (64 lanes).
 __device__ inline int wave_incl_scan(int v, int lane) {
 #pragma unroll

@@ -39,13 +39,12 @@ __global__ __launch_bounds__(256) void delta_post_kernel(PageScoreArgs a, int n_
   const int h_lo = g_lo * G, h_hi = g_hi * G;
   if ((int)blockIdx.x >= n_chunks) {
     const int h = h_lo + 4 * ((int)blockIdx.x - n_chunks) + wave;
-    if (h < h_hi) combine_head<ESZ, D>(a.cb, h, b, lane);
+    if (h < h_hi) combine_head<ESZ, D, 32>(a.cb, h, b, lane);
     return;
   }
   for (int h = h_lo + wave; h < h_hi; h += 4) {
     float M, L;
-    merge_split_stats(a.cb.ml_part + ((int64_t)b * a.hq + h) * a.cb.s_cap * 2, combine_splits(a.cb, b, h / G),
-                      lane, M, L);
+    head_split_stats(a.cb, b, h, lane, M, L);
     if (lane == 0) lse2_s[h - h_lo] = (L > 0.f) ? M + log2f(L) : -INFINITY;
   }
   __syncthreads();
