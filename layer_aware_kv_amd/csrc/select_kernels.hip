@@ -82,15 +82,27 @@ __global__ __launch_bounds__(256) void delta_post_kernel(PageScoreArgs a, int n_
         const int64_t blk = ((int64_t)b * a.hkv + g) * nsub + t / 16;
         const uint16_t* up = a.rel_w + blk * Gp * 16 + (t % 16);
         const float* rp = a.rel_max + blk * Gp;
-        for (int h = 0; h < G; ++h) {
-          const u32x2 w = *reinterpret_cast<const u32x2*>(up + h * 16);
-          const float c = exp2f(rp[h] - lse2_s[g * G + h - h_lo]);
-          const float u[4] = {(float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] & 0xFFFFu)),
-                              (float)__builtin_bit_cast(_Float16, (uint16_t)(w[0] >> 16)),
-                              (float)__builtin_bit_cast(_Float16, (uint16_t)(w[1] & 0xFFFFu)),
-                              (float)__builtin_bit_cast(_Float16, (uint16_t)(w[1] >> 16))};
+        // every head's weights and maximum are loaded before the first is used (G <= 16)
+        u32x2 w[16];
+        float rh[16];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] = fmaxf(acc[e], (t + e < T) ? u[e] * c : 0.f);
+        for (int h = 0; h < 16; ++h) {
+          if (h < G) {
+            w[h] = *reinterpret_cast<const u32x2*>(up + h * 16);
+            rh[h] = rp[h];
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < 16; ++h) {
+          if (h < G) {
+            const float c = exp2f(rh[h] - lse2_s[g * G + h - h_lo]);
+            const float u[4] = {(float)__builtin_bit_cast(_Float16, (uint16_t)(w[h][0] & 0xFFFFu)),
+                                (float)__builtin_bit_cast(_Float16, (uint16_t)(w[h][0] >> 16)),
+                                (float)__builtin_bit_cast(_Float16, (uint16_t)(w[h][1] & 0xFFFFu)),
+                                (float)__builtin_bit_cast(_Float16, (uint16_t)(w[h][1] >> 16))};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaxf(acc[e], (t + e < T) ? u[e] * c : 0.f);
+          }
         }
       }
     }
