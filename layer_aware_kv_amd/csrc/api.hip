@@ -40,6 +40,11 @@ lak_status hip_fail(hipError_t e, const char* where) {
 // is given.
 constexpr int kTargetWgs = 1024;
 constexpr int kTargetWgsDelta = 1536;  // smaller delta splits spread the scratch writes
+// Ragged batches (the longest row more than 1.1x the mean) on the full and delta tiers:
+// splits of a uniform batch end together in one workgroup round, those of unequal rows
+// do not, and smaller splits then keep the CUs busy to the end (workload of 32 rows of
+// 256-1024 pages: full 448 -> 410 us, delta 486 -> 467 us).
+constexpr int kTargetWgsRagged = 3072;
 constexpr int kMinSubtilesPerWg = 8;
 // Each of the 4 waves of a decode workgroup keeps the page ids of its items in one
 // register per lane (two for the full tier), so a split holds at most 4 * 64 items
@@ -80,6 +85,11 @@ int lak::tune_target_wgs(int mode) {
   static const int sparse = env_int("LAK_TUNE_SPARSE_WGS", kTargetWgs, 64, 65536);
   static const int delta = env_int("LAK_TUNE_DELTA_WGS", kTargetWgsDelta, 64, 65536);
   return mode == MODE_SPARSE ? sparse : (mode == MODE_DELTA ? delta : full);
+}
+
+int lak::tune_ragged_wgs() {
+  static const int v = env_int("LAK_TUNE_RAGGED_WGS", kTargetWgsRagged, 64, 65536);
+  return v;
 }
 
 int lak::tune_min_subtiles() {
@@ -159,8 +169,9 @@ WsLayout ws_layout(const lak_cache* c) {
 // rows (per-row item counts summed: a ragged batch gives its long rows more splits),
 // `max_items` the longest row's count and `max_splits` the most splits a row may use
 // (the partial buffers hold max_splits per row).
-int plan_pps(int64_t work, int max_items, int max_splits, int subtiles_per_page, int mode) {
-  const int target = tune_target_wgs(mode);
+int plan_pps(int64_t work, int max_items, int max_splits, int subtiles_per_page, int mode, bool ragged) {
+  const int target = (ragged && mode != MODE_SPARSE) ? std::max(tune_ragged_wgs(), tune_target_wgs(mode))
+                                                     : tune_target_wgs(mode);
   int pps = (int)((work + target - 1) / target);
   pps = std::max(pps, (max_items + max_splits - 1) / std::max(max_splits, 1));
   const int min_sub = tune_min_subtiles();
@@ -221,7 +232,9 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
     max_items = std::max(max_items, items);
     work += (int64_t)items * d.num_kv_heads;
   }
-  const int pps = plan_pps(work, max_items, c->s_cap / std::max(c->batch, 1), spp, mode);
+  // ragged: the longest row holds more than 1.1x the mean row's items
+  const bool ragged = (int64_t)max_items * c->batch * d.num_kv_heads * 10 > work * 11;
+  const int pps = plan_pps(work, max_items, c->s_cap / std::max(c->batch, 1), spp, mode, ragged);
   const int splits = (max_items + pps - 1) / pps;
   if ((int64_t)splits * c->batch > c->s_cap)
     return fail(LAK_EINVAL, "internal: %d splits x %d rows exceed capacity %d", splits, c->batch, c->s_cap);
@@ -375,8 +388,9 @@ lak_status lak_cache_create(const lak_cache_desc* desc, lak_cache** out) {
   // at most M items) S <= target / R + 1, and with pps capped at kMaxItemsPerSplit
   // S <= M / kMaxItemsPerSplit + 1.
   {
-    const int tmax = std::max(std::max(tune_target_wgs(MODE_FULL), tune_target_wgs(MODE_SPARSE)),
-                              tune_target_wgs(MODE_DELTA));
+    const int tmax = std::max(std::max(std::max(tune_target_wgs(MODE_FULL), tune_target_wgs(MODE_SPARSE)),
+                                       tune_target_wgs(MODE_DELTA)),
+                              tune_ragged_wgs());
     c->s_cap = (tmax + d.num_kv_heads - 1) / d.num_kv_heads +
                d.max_batch * ((d.max_pages_per_seq + kMaxItemsPerSplit - 1) / kMaxItemsPerSplit + 2);
   }

@@ -102,6 +102,7 @@ struct KvGeom {
 //   LAK_TUNE_TARGET_WGS    workgroups a full / delta split-K launch aims for
 //   LAK_TUNE_SPARSE_WGS    workgroups a sparse split-K launch aims for
 //   LAK_TUNE_DELTA_WGS     workgroups a delta split-K launch aims for (default 1536)
+//   LAK_TUNE_RAGGED_WGS    workgroups a full / delta launch over a ragged batch aims for (3072)
 //   LAK_TUNE_DELTA_LDS     1 (default): delta scratch staged in LDS, written at a split's end
 //   LAK_TUNE_MIN_SUBTILES  fewest 16-token sub-tiles a split-K workgroup is given (default 8)
 int tune_decode_batch(int mode);
@@ -112,6 +113,7 @@ inline size_t delta_stage_bytes(int pps, int page, int G) {
   return (size_t)pps * (page / 16) * gp * (16 * 2 + 4);
 }
 int tune_target_wgs(int mode);
+int tune_ragged_wgs();
 int tune_delta_lds();
 int tune_min_subtiles();
 
