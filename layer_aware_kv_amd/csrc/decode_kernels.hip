@@ -89,18 +89,21 @@ struct Frag<2, D> {
       for (int i = 0; i < NL; ++i) k[i] = *reinterpret_cast<const u32x4*>(kr + (4 * i + j) * 8);
     }
     if (j == tt / 4) {
+      uint32_t val[NL][2];  // every load issued before the first is used
 #pragma unroll
       for (int i = 0; i < NL; ++i)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t val = vr[16 * (2 * i + h) + n];
+        for (int h = 0; h < 2; ++h) val[i][h] = vr[16 * (2 * i + h) + n];
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int e = 0; e < 4; ++e)  // compile-time element index
             if (e == (tt & 3)) {
               const int x = h * 4 + e, sh = 16 * (x & 1);
-              v[i][x >> 1] = (v[i][x >> 1] & ~(0xFFFFu << sh)) | (val << sh);
+              v[i][x >> 1] = (v[i][x >> 1] & ~(0xFFFFu << sh)) | (val[i][h] << sh);
             }
-        }
     }
   }
   __device__ inline void pv(f32x4* o, const float* p) const {
@@ -168,11 +171,14 @@ struct Frag<4, D> {
       for (int i = 0; i < NL; ++i) k[i] = *reinterpret_cast<const u32x4*>(kr + (4 * i + j) * 4);
     }
     if (j == tt / 4) {
+      uint32_t val[NL];  // every load issued before the first is used
+#pragma unroll
+      for (int i = 0; i < NL; ++i) val[i] = vr[16 * i + n];
 #pragma unroll
       for (int i = 0; i < NL; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e)  // compile-time element index (a runtime one goes to scratch)
-          if (e == (tt & 3)) v[i][e] = vr[16 * i + n];
+          if (e == (tt & 3)) v[i][e] = val[i];
     }
   }
   __device__ inline void pv(f32x4* o, const float* p) const {
@@ -304,7 +310,8 @@ __global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) v
   }
   // Fused append: split 0 of each (b, g) writes this step's token at T-1 into the
   // pool for later calls; the wave that attends over that sub-tile in this call
-  // takes the token from k_new / v_new directly (`patch`; fp8 pools: see `issue`).
+  // stores the same bytes itself before its loads (below), or, on the delta tier of
+  // bfloat16 / fp32 pools, patches the token into its fragments (`patch`).
   // (fp8 pools: rows arrive as bfloat16 and are encoded with their row scale.)
   const QE* krow_new = nullptr;
   const QE* vrow_new = nullptr;
@@ -387,11 +394,14 @@ __global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) v
   // that reading them inside the loop never waits on the K/V loads in flight.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-  if constexpr (ESZ == 1) {
-    // fp8 fused append: the wave whose items include the page of this step's token
-    // encodes and stores that row itself (the same bytes split 0 writes) before any
-    // of its loads, so it then reads the token from the pool like any other; the
-    // workgroup-scope fence orders its lanes' stores before those loads.
+  // The wave whose items include the page of this step's token stores that row itself
+  // (the same bytes split 0 writes; fp8 pools: encoded) before any of its loads, so it
+  // then reads the token from the pool like any other; the workgroup-scope fence orders
+  // its lanes' stores before those loads.  This keeps the sub-tile loop free of the
+  // register patch, whose extra loads force conservative wait counts on every sub-tile
+  // (full tier 332 -> 324 us at B 16, T 64k); the delta tier of bfloat16 / fp32 pools
+  // keeps the patch, which measured faster there (372 vs 381 us).
+  if constexpr (ESZ == 1 || MODE != MODE_DELTA) {
     if (krow_new != nullptr) {
       unsigned long long own = 0ull;
       int k_own = 0;
@@ -408,9 +418,16 @@ __global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) v
         const int tin = (T - 1) % P;
         const int64_t row0 = (phys * a.hkv + g) * P + (tin / kSub) * kSub;
         const int tt = tin % kSub;
-        encode_rows_fp8(D, const_cast<E*>(kpool) + row0 * D, const_cast<E*>(vpool) + row0 * D, tt,
-                        const_cast<float*>(a.k_scale) + row0 + tt, const_cast<float*>(a.v_scale) + row0 + tt,
-                        krow_new, vrow_new, lane);
+        if constexpr (ESZ == 1) {
+          encode_rows_fp8(D, const_cast<E*>(kpool) + row0 * D, const_cast<E*>(vpool) + row0 * D, tt,
+                          const_cast<float*>(a.k_scale) + row0 + tt, const_cast<float*>(a.v_scale) + row0 + tt,
+                          krow_new, vrow_new, lane);
+        } else {
+          for (int d = lane; d < D; d += 64) {
+            const_cast<E*>(kpool)[row0 * D + k_off<ESZ>(tt, d)] = krow_new[d];
+            const_cast<E*>(vpool)[row0 * D + v_off<ESZ>(tt, d)] = vrow_new[d];
+          }
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       }
@@ -446,7 +463,7 @@ __global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) v
   for (int x = 0; x < F::NO; ++x) o[x] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   auto process = [&](F& f, int ct, int x) {
-    if constexpr (ESZ != 1) {
+    if constexpr (ESZ != 1 && MODE == MODE_DELTA) {
       if (krow_new != nullptr && T - 1 < ct + kSub) f.patch(krow_new, vrow_new, (T - 1) - ct, lane);
     }
     const f32x4 sacc = f.qk(qf);
