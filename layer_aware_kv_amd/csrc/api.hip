@@ -271,7 +271,7 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
   a.rel_max = reinterpret_cast<float*>(wsb + w.rel_max);
   {
     const int G = d.num_q_heads / d.num_kv_heads;
-    const size_t staged = delta_stage_bytes(pps, d.page_size, G);
+    const size_t staged = delta_stage_bytes(pps, d.page_size, G, agg == LAK_AGG_SUM);
     a.lds_stage = (mode == MODE_DELTA && tune_delta_lds() && staged <= 64 * 1024) ? 1 : 0;
     a.sum_pairs = (mode == MODE_DELTA && agg == LAK_AGG_SUM) ? 1 : 0;
   }

@@ -502,9 +502,15 @@ __global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) v
       }
       e = xor32_add(xor16_add(e));
       if (head_ok && j == 0) {
-        const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + ct / kSub;
         typedef float f32x2 __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<f32x2*>(a.pairs + (blk * Gp + n) * 2) = (f32x2){mx, e};
+        if (a.lds_stage) {
+          // staged at the sub-tile's index within the workgroup; flushed at the end
+          const int li = (wave + kWaves * (x / spp)) * spp + (x % spp);
+          *reinterpret_cast<f32x2*>(lds + (li * Gp + n) * 2) = (f32x2){mx, e};
+        } else {
+          const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + ct / kSub;
+          *reinterpret_cast<f32x2*>(a.pairs + (blk * Gp + n) * 2) = (f32x2){mx, e};
+        }
       }
     } else if (MODE == MODE_DELTA && n < Gp) {
       // MAX aggregation: this head's max logit r over the sub-tile (log2 units, exact)
@@ -589,6 +595,24 @@ __global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) v
     }
     __syncthreads();  // the merge below reuses this LDS
   }
+  if (MODE == MODE_DELTA && a.lds_stage && a.sum_pairs) {
+    // SUM: the workgroup's (max, sum) pairs, 16-byte units (two heads each); a padding
+    // head's pair is never read
+    __syncthreads();
+    const int n_sub = n_split * spp;
+    const int upb = Gp / 2;  // units per sub-tile block
+    for (int idx = threadIdx.x; idx < n_sub * upb; idx += blockDim.x) {
+      const int li = idx / upb, u = idx - li * upb;
+      const int member = li / spp, sub = li - member * spp;
+      const int t0 = (s + S_row * member) * P + sub * kSub;
+      if (t0 < T) {
+        const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + t0 / kSub;
+        *reinterpret_cast<u32x4*>(a.pairs + blk * Gp * 2 + 4 * u) =
+            *reinterpret_cast<const u32x4*>(lds + li * Gp * 2 + 4 * u);
+      }
+    }
+    __syncthreads();  // the merge below reuses this LDS
+  }
 
   l = xor32_add(xor16_add(l));
 
@@ -652,8 +676,8 @@ static hipError_t launch_decode_t(int mode, const DecodeArgs& a, int splits, int
                                   hipStream_t st) {
   const int G = a.hq / a.hkv;
   size_t lds = (size_t)(kWaves * G * D + 2 * kWaves * 16) * sizeof(float);
-  if (mode == MODE_DELTA && a.lds_stage && !a.sum_pairs)
-    lds = std::max(lds, delta_stage_bytes(a.pps, a.page, G));
+  if (mode == MODE_DELTA && a.lds_stage)
+    lds = std::max(lds, delta_stage_bytes(a.pps, a.page, G, a.sum_pairs != 0));
   dim3 grid(splits, a.hkv, batch);
   // fp32 pools always load one sub-tile at a time: their fragments fill the register
   // budget of a deeper batch.

@@ -35,7 +35,7 @@ struct DecodeArgs {
   // over the sub-tile (log2 units) and every token's relative weight 2^(logit - r) in fp16:
   uint16_t* rel_w;             // [B][Hkv][t_pad/16][Gp][16] fp16 (Gp = G rounded up to even)
   float* rel_max;              // [B][Hkv][t_pad/16][Gp]
-  int lds_stage;               // delta tier: stage them in LDS and write them at the split's end
+  int lds_stage;               // delta tier: stage the scratch in LDS, write it at the split's end
   float* pairs;                // delta tier, SUM aggregation: per (head, sub-tile) the pair
   int sum_pairs;               // (max logit in log2 units, sum of 2^(logit - max)) [..][Gp][2]
   int64_t t_pad;               // token capacity of a sequence (max_pages * page)
@@ -107,10 +107,11 @@ struct KvGeom {
 //   LAK_TUNE_MIN_SUBTILES  fewest 16-token sub-tiles a split-K workgroup is given (default 8)
 int tune_decode_batch(int mode);
 
-// LDS bytes of a delta split's staged blocks (fp16 weights + float maxima per sub-tile).
-inline size_t delta_stage_bytes(int pps, int page, int G) {
+// LDS bytes of a delta split's staged blocks: MAX, fp16 weights + float maxima per
+// (head, sub-tile); SUM, the (max, sum) pair.
+inline size_t delta_stage_bytes(int pps, int page, int G, bool sum = false) {
   const size_t gp = (size_t)(G + (G & 1));
-  return (size_t)pps * (page / 16) * gp * (16 * 2 + 4);
+  return (size_t)pps * (page / 16) * gp * (sum ? 2 * 4 : 16 * 2 + 4);
 }
 int tune_target_wgs(int mode);
 int tune_ragged_wgs();
