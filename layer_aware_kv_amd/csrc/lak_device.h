@@ -73,7 +73,6 @@ __device__ inline float xor32_add(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ inline int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, 64); }
 
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
   uint32_t b = __float_as_uint(f);
