@@ -202,6 +202,40 @@ def test_kv_prefill_append_gather_roundtrip(dtype, D, P):
     assert torch.equal(kg[0], kr[0])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("agg", ["max", "sum"])
+def test_delta_and_sparse_wide_logit_range(dtype, agg):
+    """Logits spread over about +-150 log2 units (q scaled by 32): many sub-tiles peak more
+    than 64 log2 units below the running maximum, so the delta kernel takes their weights
+    from the logits directly rather than from the probabilities, and the page scores of
+    most pages underflow float32 (scored as tied at 0 by the selection band)."""
+    B, HQ, HKV, D, P = 2, 28, 4, 128, 16
+    case = random_case(31, B, HQ, HKV, D, [1500, 777], dtype, q_scale=32.0)
+    sm = float(1.0 / np.sqrt(D))
+    cache = make_cache(case, P)
+    q = fill_and_step(cache, case)
+    k_top, rec = 20, 2
+    scores = torch.full((B, HKV, cache.max_pages), -7.0, dtype=torch.float32, device="cuda")
+    out, lse, sel, cnt = cache.attn_delta_select(0, q, sm, k_top, rec, agg, "group", page_scores=scores)
+    out_s, lse_s = cache.attn_sparse(0, q, sm, sel, cnt)
+    torch.cuda.synchronize()
+    for b, T in enumerate(case.lengths):
+        K, V = case.K[b, :, :T], case.V[b, :, :T]
+        r = oracle.delta_layer(case.q[b], K, V, sm, P, k_top, rec, agg, "group")
+        assert_close(host(out[b]), r["out"], TOL[dtype], f"out b={b}")
+        assert_close(host(lse[b]), r["lse"], LSE_TOL[dtype], f"lse b={b}")
+        NP = -(-T // P)
+        np.testing.assert_allclose(scores[b].cpu().numpy().astype(np.float64)[:, :NP], r["page_scores"],
+                                   rtol=SCORE_RTOL[agg], atol=1e-7)
+        for g in range(HKV):
+            check_selection(sel[b, g].cpu().numpy(), int(cnt[b, g]), r["page_scores"][g], k_top, rec,
+                            sel.shape[-1])
+        sels = [sel[b, g, :int(cnt[b, g])].cpu().tolist() for g in range(HKV)]
+        ref, ref_lse = oracle.sparse_attention(case.q[b], K, V, sels, P, sm)
+        assert_close(host(out_s[b]), ref, TOL[dtype], f"sparse b={b}")
+        assert_close(host(lse_s[b]), ref_lse, LSE_TOL[dtype], f"sparse lse b={b}")
+
+
 def test_edge_cases_empty_and_degenerate():
     from layer_aware_kv_amd import PagedKVCache
     # a sequence of length 0 (no decode step yet): out = 0, lse = -inf
