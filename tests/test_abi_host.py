@@ -194,3 +194,15 @@ def test_header_is_plain_c():
         r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
                             "-I", os.path.join(ROOT, "include"), path], capture_output=True, text=True)
         assert r.returncode == 0, r.stderr
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU's share; a request for several exits with a message
+    (before touching any GPU) instead of reporting a number it did not measure."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
