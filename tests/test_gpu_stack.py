@@ -23,7 +23,8 @@ SAMPLES = {
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,kv", [("stack28_b8_t16k", None), ("stack28_b16_t64k", None),
-                                     ("stack36_b32_t8k_32k", None), ("stack28_b16_t64k", "fp8")])
+                                     ("stack36_b32_t8k_32k", None), ("stack28_b16_t64k", "fp8"),
+                                     ("stack36_b32_t8k_32k", "fp8")])
 def test_stack_full_size_sampled(name, kv):
     import bench
     from oracle.quant import quantize_dequantize
