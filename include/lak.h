@@ -172,8 +172,8 @@ lak_status lak_kv_gather_scales(lak_cache* cache, int32_t layer, int32_t b, int3
  * p = softmax(sm_scale * <q[b][h], k_t>).  Split-K over pages plus a combine kernel.
  * k_new, v_new (both NULL, or both device [B][Hkv][D]): this step's key and value;
  * when given, the call also appends them at position T_b - 1, exactly as
- * lak_kv_append would before the call (one launch fewer; for an fp8 cache the
- * call enqueues that append kernel itself).  The same holds for the
+ * lak_kv_append would before the call, inside its own decode kernel (one launch
+ * fewer; fp8 caches encode the bfloat16 rows there).  The same holds for the
  * k_new / v_new arguments of lak_attn_delta_select and lak_attn_sparse.
  * lse may be NULL.  ws: lak_workspace_bytes() bytes of device memory. */
 lak_status lak_attn_full(lak_cache* cache, int32_t layer, const void* q, const void* k_new,
