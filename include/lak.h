@@ -5,11 +5,12 @@
  * Long-Context Reasoning" (AI summary page, "Methodology in Plain English" and
  * "Main Findings").  A model's layers are split into three tiers that share one
  * paged KV cache kept whole in HBM (DELTA never evicts tokens):
- *   - full layers (layers 0 and 1) run ordinary full decode attention;
- *   - delta-layers run full attention, take for every token the maximum softmax
- *     weight across heads, sum those scores per page, keep the most recent pages
- *     and fill the rest of the budget with the highest-scoring older pages;
- *   - sparse layers attend only to the tokens of the latest selection.
+ *   - full layers (the first two) attend to the whole context;
+ *   - delta-layers also attend to the whole context and, from those softmax
+ *     weights, score each token by its largest weight over the heads, score each
+ *     page by adding its tokens' scores, and choose pages: a window of the newest
+ *     pages plus, up to the budget, the older pages with the largest scores;
+ *   - sparse layers attend to the tokens of the most recent choice only.
  *
  * Conventions shared by every entry point
  *   - Pointers named "device" point to HIP device memory owned by the caller; the
@@ -60,7 +61,8 @@ typedef enum {
 typedef enum { LAK_BF16 = 0, LAK_F32 = 1, LAK_FP8_E4M3 = 2 } lak_dtype;
 
 /* Head aggregation of per-token scores in a delta-layer.  MAX is the pages' rule
- * (maximum attention weight across heads); SUM adds the weights instead. */
+ * (a token's score is its largest weight over the heads); SUM adds the weights
+ * instead. */
 typedef enum { LAK_AGG_MAX = 0, LAK_AGG_SUM = 1 } lak_agg;
 
 /* Which heads a delta-layer aggregates.  GROUP: the G query heads of each KV head,
@@ -167,8 +169,8 @@ lak_status lak_kv_gather(lak_cache* cache, int32_t layer, int32_t b, int32_t g, 
 lak_status lak_kv_gather_scales(lak_cache* cache, int32_t layer, int32_t b, int32_t g, int32_t t0,
                                 int32_t n, float* k_out, float* v_out, void* stream);
 
-/* Full decode attention of layer `layer` (layers 0-1 and delta-layers: "run
- * ordinary full attention"): out[b][h] = sum_t p_t v_t over t < T_b with
+/* Full decode attention of layer `layer` (layers 0-1 and delta-layers attend to
+ * the whole context): out[b][h] = sum_t p_t v_t over t < T_b with
  * p = softmax(sm_scale * <q[b][h], k_t>).  Split-K over pages plus a combine kernel.
  * k_new, v_new (both NULL, or both device [B][Hkv][D]): this step's key and value;
  * when given, the call also appends them at position T_b - 1, exactly as
@@ -184,7 +186,7 @@ lak_status lak_attn_full(lak_cache* cache, int32_t layer, const void* q, const v
  * selection it installs.  Per token t < T_b: a_t = AGG over the scope's heads of
  * exp(logit_{h,t} - lse_h); page score S_j = sum of a_t over the valid tokens of
  * page j.  Selection per row (row = (b, kv head) for GROUP, b for ALL): the last
- * `recency` pages, plus the `k_top` highest-scoring older pages (ties: lower page
+ * `recency` pages, plus the `k_top` older pages of largest score (ties: lower page
  * index first), written as ascending logical page ids to
  * sel[row][0 .. count), -1 after; sel_count[row] = count = min(NP_b, k_top + recency).
  * sel: device int32 [B][R][sel_capacity], R = Hkv (GROUP) or 1 (ALL),
@@ -217,9 +219,9 @@ lak_status lak_attn_sparse(lak_cache* cache, int32_t layer, const void* q, const
                            const int32_t* sel_count, int32_t sel_capacity, int32_t scope, void* out,
                            float* lse, void* ws, size_t ws_bytes, void* stream);
 
-/* One decode step of a whole attention stack (the three-tier schedule: "Methodology
- * in Plain English" -- full layers, delta-layers that refresh the page selection,
- * sparse layers over the latest selection, recomputed for every generated token).
+/* One decode step of a whole attention stack (the three-tier schedule of
+ * "Methodology in Plain English": full layers, delta-layers that renew the page
+ * choice, sparse layers over the most recent choice, renewed at every token).
  * Performs lak_step_begin, then for every layer l in order: the attention call of
  * its tier (full / delta-select / sparse with the selection of the latest
  * delta-layer before l), appending k_new[l] / v_new[l] inside the call.  All host

@@ -1,7 +1,7 @@
 // Delta-layer page scoring and page selection ("Methodology in Plain English",
 // DELTA AI summary page): per token, the maximum (or sum) over the scope's heads of
 // the softmax weight exp(logit - lse); per page, the sum over its valid tokens;
-// then the last `recency` pages plus the `k_top` highest-scoring older pages.  The
+// then the last `recency` pages plus the `k_top` older pages of largest score.  The
 // scoring launch also combines the delta decode's split partials into the layer's
 // attention output.
 #include <math.h>

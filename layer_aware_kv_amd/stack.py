@@ -1,10 +1,10 @@
 """Decode-step driver over a layer stack (the three-tier schedule of DELTA).
 
-"Methodology in Plain English" (DELTA AI summary page): layers 0 and 1 run full
-attention, a few delta-layers run full attention and refresh the page selection,
-every other layer runs sparse attention over the latest selection; the selection
-is recomputed for every generated token.  "Main Findings": layer 2 is always the
-first delta-layer.
+"Methodology in Plain English" (DELTA AI summary page): the first two layers and a
+few delta-layers attend to the whole context, the delta-layers renewing the page
+choice; the other layers attend to the most recent choice, which is renewed for
+every generated token.  "Main Findings": the first delta-layer is layer 2 in every
+model.
 """
 from __future__ import annotations
 

@@ -6,14 +6,14 @@ the library under ``layer_aware_kv_amd/`` never does, and shares no code with it
 
 Source of the definitions: "DELTA: Dynamic Layer-Aware Token Attention for
 Efficient Long-Context Reasoning", AI summary page, sections "Methodology in
-Plain English" (three layer tiers; delta-layers run full attention, take the
-per-token maximum attention weight across heads, group tokens into fixed-size
-pages, sum the per-token scores in a page, keep the most recent pages and fill
-the rest of the budget with the highest-scoring older pages; sparse layers
-attend only to the selected pages; selections refreshed at each delta-layer and
-for every generated token; full KV cache kept; page size 16) and "Main Findings"
-(budget K pages plus a recency window of L pages; layers 0 and 1 full, layer 2
-the first delta-layer).
+Plain English" (three layer tiers; a delta-layer attends to the whole context,
+scores each token by its largest softmax weight over the heads, scores each
+page of 16 tokens by adding its tokens' scores, and chooses a window of the
+newest pages plus, up to the budget, the older pages of largest score; the
+other layers attend to the chosen pages only; the choice is renewed at every
+delta-layer and for every generated token; no token leaves the KV cache) and
+"Main Findings" (budget of K pages plus a window of L recent pages; the first
+two layers attend fully and the first delta-layer is layer 2).
 
 Everything is plain NumPy in float64, one (batch row, head) at a time, in the
 order the pages state the steps.  Readings of points the pages leave open are

@@ -1,10 +1,10 @@
 """Full and sparse decode attention, float64 (oracle; test infrastructure only).
 
 Full attention is what layers 0-1 and every delta-layer compute ("Methodology in
-Plain English": early layers run ordinary full attention; delta-layers also run
-full attention).  Sparse attention is the same softmax attention restricted to
-the tokens of the selected pages ("attending only to the tokens in those
-selected pages"); the softmax renormalises over those tokens.
+Plain English": the early layers and the delta-layers attend to the whole
+context).  Sparse attention is the same softmax attention restricted to the
+tokens of the chosen pages (same section); the softmax renormalises over those
+tokens.
 
 Readings where the pages are silent:
 * grouped-query attention: query head h reads KV head g(h) = floor(h / G),

@@ -2,11 +2,11 @@
 
 Steps, in the order of "Methodology in Plain English" on the DELTA AI summary page:
 1. full attention of the delta-layer gives each head's softmax weights p[h, t];
-2. per-token score: the maximum attention weight across heads;
+2. per-token score: the token's largest softmax weight over the heads;
 3. tokens are grouped into fixed-size pages (page size P);
 4. page score: sum of the per-token scores of the page;
 5. the most recent pages are kept as a recency window (L pages, "Main Findings");
-6. the rest of the budget (K pages) is filled with the highest-scoring older pages.
+6. the remaining budget (K pages) goes to the older pages of largest score.
 
 Readings where the pages are silent, ambiguous or at odds:
 * heads aggregated (scope "group"): the query heads of one KV group, giving one

@@ -1,9 +1,9 @@
 """fp8 KV pages: E4M3 codes with one float32 scale per (token, KV head) row.
 Oracle; test infrastructure only.
 
-The pages list quantization as a technique to combine with DELTA so that it cuts
-memory as well as compute (DELTA AI summary page, "Future Directions"); they fix
-no format.  Format: OCP 8-bit floating point, E4M3 variant (1 sign bit, 4
+The pages name quantization as a technique to pair with DELTA, to save memory on
+top of DELTA's savings in attention work (DELTA AI summary page, "Future
+Directions"); they fix no format.  Format: OCP 8-bit floating point, E4M3 variant (1 sign bit, 4
 exponent bits with bias 7, 3 mantissa bits; no infinities; S.1111.111 is NaN;
 largest finite magnitude 448; subnormals M/8 * 2^-6).
 

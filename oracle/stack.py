@@ -1,10 +1,10 @@
 """One decode step through a layer stack (oracle; test infrastructure only).
 
-"Methodology in Plain English" (DELTA AI summary page): layers 0 and 1 run full
-attention; a small set of delta-layers run full attention and refresh the page
-selection; every remaining layer runs sparse attention over the selection of the
-latest delta-layer, recomputed for every generated token.  "Main Findings":
-layers 0 and 1 are always full and layer 2 is always the first delta-layer.
+"Methodology in Plain English" (DELTA AI summary page): the first two layers
+attend to the whole context; a few delta-layers do too and renew the page choice;
+the other layers attend to the pages chosen by the most recent delta-layer, a
+choice renewed for every generated token.  "Main Findings": the first two layers
+are full in every model and the first delta-layer is layer 2.
 
 Readings: a delta-layer's attention output is its full-attention output (the
 selection is a side output); a sparse layer that comes before any delta-layer in

@@ -19,7 +19,7 @@ def test_tiers_from_pages_delta_lists():
         deltas = [int(x) for x in lst.split(",")]
         tiers = oracle.layer_tiers(int(n), [0, 1], deltas)
         assert tiers[0] == tiers[1] == "full"
-        assert tiers[2] == "delta"          # layer 2 is always the first delta-layer
+        assert tiers[2] == "delta"          # the first delta-layer is layer 2 (Main Findings)
         assert [i for i, t in enumerate(tiers) if t == "delta"] == deltas
         assert tiers.count("sparse") == int(n) - 2 - len(deltas)
 
@@ -30,8 +30,8 @@ def _stack_inputs(rng, n_layers, hq, hkv, T, D):
 
 
 def test_all_delta_stack_equals_all_full():
-    # "as the count [of delta-layers] approaches the total number of layers, DELTA reduces
-    # to full attention" (Main Findings)
+    # with every layer a delta-layer (or full), DELTA is full attention (Main Findings:
+    # runtime tends to full attention's as the delta-layer count nears the layer count)
     rng = np.random.default_rng(1)
     inputs = _stack_inputs(rng, 6, 8, 2, 300, 32)
     full = oracle.stack_step(["full"] * 6, inputs, 1.0, 16, 2, 1)
@@ -73,7 +73,7 @@ def test_sparse_before_delta_is_an_error():
 
 def test_no_eviction_dropped_page_can_return():
     # the full cache stays; a page unselected at one step is selectable at the next
-    # ("Methodology in Plain English": DELTA never removes tokens from the KV cache)
+    # ("Methodology in Plain English": no token is dropped from the KV cache)
     rng = np.random.default_rng(8)
     hq, hkv, T, D = 4, 1, 16 * 10, 16
     K = rng.standard_normal((hkv, T, D)) * 0.05
