@@ -15,8 +15,8 @@ namespace lak {
 // Delta-layer post step, one launch.  Grid (n_chunks + combine blocks, score rows R,
 // batch).  Blocks x < n_chunks score pages of row (b, r); the others combine the split
 // partials of the row's heads (one head per wave: out and lse of the layer).  A scoring
-// block first merges, from the same partials and with the same routine as the combine
-// (merge_split_stats), the log-sum-exp of each head it aggregates.
+// block first merges, from the same partials and with the combine's own statistics
+// routine (head_split_stats), the log-sum-exp of each head it aggregates.
 //
 // MAX (SUMP false): a block takes `tokens_per_block` consecutive tokens of its row, 4
 // per thread, so a page of P tokens is P/4 adjacent lanes and its sum is a butterfly
