@@ -173,6 +173,143 @@ class StackBench:
         return time.perf_counter() - t0
 
 
+def traffic_for(wl, dom, kv_dtype):
+    """Counter-measured HBM bytes per launch of the dominant kernel, from the committed
+    counter summary, while the kernel sources still hash to the value it was taken on."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tj = json.load(f)
+        ent = tj.get("kernels", {}).get(dom)
+        if (tj.get("source_hash") == kernel_source_hash() and tj.get("workload") == wl.name and ent
+                and tj.get("kv_dtype", wl.dtype) == kv_dtype):
+            return ent["hbm_bytes_per_launch"], (f"profiles/traffic.json: rocprofv3 FETCH_SIZE / WRITE_SIZE "
+                                                 f"counters taken on kernel sources {tj['source_hash']} "
+                                                 f"(the current ones), not in this run")
+    except (OSError, ValueError, KeyError):
+        pass
+    return None, None
+
+
+def measure_stack(torch, wl, W, K, agg="max", scope="group", kv_dtype=None, keep=False):
+    """Times one stack workload: the DELTA stack (value), a per-tier pass with events on
+    every decode kernel, and the same stack with every layer full.  Returns the summary
+    and, with ``keep``, the StackBench (for the fidelity pass)."""
+    from layer_aware_kv_amd import accounting as acc
+    from layer_aware_kv_amd._lib import event_elapsed_ms
+
+    B, L, HQ, HKV, D, P = wl.batch, wl.num_layers, wl.hq, wl.hkv, wl.d, wl.page
+    e = 2 if wl.dtype == "bf16" else 4
+    kv_dtype = kv_dtype or wl.dtype
+    kv_row = acc.kv_row_bytes(D, kv_dtype)
+    t_setup = time.perf_counter()
+    sb = StackBench(wl, W, K, agg=agg, scope=scope, kv_dtype=kv_dtype)
+    lens0, tiers = sb.lens0, sb.tiers
+    pool_gb = 2 * L * sb.cache.k_pools[0].numel() * sb.cache.k_pools[0].element_size() / 1e9
+    log(f"{wl.name}: set-up {time.perf_counter() - t_setup:.1f} s, {pool_gb:.1f} GB of {kv_dtype} KV pools, "
+        f"W={W} K={K}, drift events at steps {sorted(sb.drift)}")
+
+    # decode-kernel bytes of one launch at step s
+    def kernel_bytes(tier, s):
+        lens = [t + s + 1 for t in lens0]
+        q_bytes = B * HQ * D * e
+        if tier == "sparse":
+            toks = sum(acc.selected_tokens(t, P, wl.k_top, wl.recency) for t in lens)
+            return toks * HKV * kv_row * 2 + q_bytes + B * HKV * (wl.k_top + wl.recency) * 4
+        return sum(lens) * HKV * kv_row * 2 + q_bytes
+
+    mid = [t + W + K // 2 + 1 for t in lens0]
+    step_bytes = acc.stack_bytes(mid, tiers, HQ, HKV, D, e, P, wl.k_top, wl.recency, kv_row)
+    present = sorted(set(tiers))
+    dom = max(present, key=lambda t: step_bytes[t])
+
+    # A: the timed DELTA stack, events on the dominant tier's decode kernels
+    trA = Tracer(torch, [dom], K * tiers.count(dom))
+    tA = sb.run(tiers, trA)
+    value = B * K / tA
+    log(f"{wl.name}: DELTA stack {tA / K * 1e3:.3f} ms/step, {value:.0f} tok/s")
+
+    def summarize(records):
+        out = {}
+        for s, layer, tier, (e0, e1) in records:
+            d = out.setdefault(tier, {"launches": 0, "ms": 0.0, "bytes": 0})
+            d["launches"] += 1
+            d["ms"] += event_elapsed_ms(e0, e1)
+            d["bytes"] += kernel_bytes(tier, s)
+        for tier, d in out.items():
+            d["us_per_launch"] = 1e3 * d["ms"] / d["launches"]
+            d["achieved_GBps"] = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+            d["bytes_per_launch"] = d["bytes"] / d["launches"]
+            d["frac_of_peak"] = d["achieved_GBps"] / PEAK_HBM_GBPS
+        return out
+
+    domA = summarize(trA.records)[dom]
+
+    # B: per-tier breakdown (events on every decode kernel)
+    trB = Tracer(torch, present, K * L)
+    sb.run(tiers, trB)
+    per_tier = summarize(trB.records)
+    for t, d in per_tier.items():
+        d["ms_per_step"] = d["ms"] / K
+    log(f"{wl.name}: tiers " + ", ".join(f"{t} {d['us_per_launch']:.1f} us {d['achieved_GBps']:.0f} GB/s"
+                                         for t, d in sorted(per_tier.items())))
+
+    # C: the same stack with every layer full, same inputs
+    tC = sb.run(["full"] * L)
+    full_value = B * K / tC
+    log(f"{wl.name}: all-full stack {tC / K * 1e3:.3f} ms/step, {full_value:.0f} tok/s")
+
+    attended_delta = acc.attended_tokens(mid, tiers, P, wl.k_top, wl.recency)
+    attended_full = acc.attended_tokens(mid, ["full"] * L, P, wl.k_top, wl.recency)
+    traffic, traffic_src = traffic_for(wl, dom, kv_dtype)
+    summary = {
+        "tokens_per_s": value,
+        "ms_per_step": tA / K * 1e3,
+        "steps": K,
+        "warmup": W,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": KERNEL_NAMES[dom].format(esz=KV_ESZ[kv_dtype]),
+            "achieved": round(domA["achieved_GBps"], 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(domA["achieved_GBps"] / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "traffic_source": traffic_src,
+            "bytes_per_launch": int(domA["bytes_per_launch"]),
+            "us_per_launch": round(domA["us_per_launch"], 2),
+            "launches": domA["launches"],
+            "timing": "HIP events attached to each launch of the kernel (its start and end)",
+        },
+        "tiers": {t: {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+                  for t, d in per_tier.items()},
+        "all_full_tokens_per_s": round(full_value, 2),
+        "all_full_ms_per_step": round(tC / K * 1e3, 4),
+        "speedup_vs_all_full": round(value / full_value, 4),
+        "attended_token_ratio": round(attended_full / attended_delta, 4),
+        "algorithmic_bytes_per_step": {t: int(v) for t, v in step_bytes.items()},
+        "stack_GBps": round(sum(step_bytes.values()) / (tA / K) / 1e9, 1),
+    }
+    if keep:
+        return summary, sb
+    del sb
+    torch.cuda.empty_cache()
+    return summary, None
+
+
+def workload_config(wl, args_agg="max", args_scope="group", kv_dtype=None):
+    return {
+        "workload": wl.name,
+        "layers": wl.num_layers, "batch": wl.batch, "context": wl.context, "q_heads": wl.hq,
+        "kv_heads": wl.hkv, "head_dim": wl.d, "page": wl.page, "top_k_pages": wl.k_top,
+        "recency_pages": wl.recency, "full_layers": list(wl.full_layers), "delta_layers": list(wl.delta_layers),
+        "ragged_min": wl.ragged_min, "agg": args_agg, "scope": args_scope, "kv_dtype": kv_dtype or wl.dtype,
+        "salient_strength": wl.salient_strength, "drift_every": wl.drift_every,
+        "parallelism": "single GPU",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,7 +318,10 @@ def main():
     ap.add_argument("--workload", default="stack28_b16_t64k", choices=STACK_WORKLOADS,
                     help="layer-stack workload (default: batch 16 at context 65536)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1, help="batch rows in the CPU oracle sample")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other stack workloads (timed after the headline one at their own steps)")
+    ap.add_argument("--no-fidelity", action="store_true", help="skip the selection-fidelity passes")
+    ap.add_argument("--cpu-rows", type=int, default=4, help="batch rows in the CPU oracle sample")
     ap.add_argument("--agg", choices=["max", "sum"], default="max",
                     help="head aggregation of the delta-layers (max: the pages' rule)")
     ap.add_argument("--scope", choices=["group", "all"], default="group",
@@ -191,6 +331,8 @@ def main():
     ap.add_argument("--salient-strength", type=float, default=None,
                     help="salient keys = strength * direction + noise (workload default 4; the fidelity study's "
                          "attention sharpness)")
+    ap.add_argument("--sharp-strength", type=float, default=10.0,
+                    help="the second, sharper salient strength of the fidelity block")
     ap.add_argument("--kv-dtype", choices=["bf16", "fp8"], default=None,
                     help="KV pool element type (default: the workload's; fp8 = E4M3 codes + per-row scales)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -213,159 +355,91 @@ def main():
               "exchange; it is measured here on one GPU's share.", file=sys.stderr)
         sys.exit(2)
 
+    import dataclasses
+
     import torch
-    from layer_aware_kv_amd import accounting as acc
-    from layer_aware_kv_amd._lib import event_elapsed_ms
     from workload import get
 
     wl = get(args.workload)
+    custom = args.delta_layers is not None or args.salient_strength is not None
     if args.delta_layers is not None:
-        import dataclasses
         wl = dataclasses.replace(wl, delta_layers=tuple(int(x) for x in args.delta_layers.split(",") if x != ""))
     if args.salient_strength is not None:
-        import dataclasses
         wl = dataclasses.replace(wl, salient_strength=args.salient_strength)
     W = wl.warmup if args.warmup is None else args.warmup
     K = wl.steps if args.steps is None else args.steps
-    B, L, HQ, HKV, D, P = wl.batch, wl.num_layers, wl.hq, wl.hkv, wl.d, wl.page
-    e = 2 if wl.dtype == "bf16" else 4
     kv_dtype = args.kv_dtype or wl.dtype
     if kv_dtype == "fp8" and wl.dtype != "bf16":
         sys.exit("fp8 pools take bfloat16 rows: use a bf16 workload")
-    kv_row = acc.kv_row_bytes(D, kv_dtype)
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
     log(f"device {props.name} ({props.multi_processor_count} CUs), workload {wl.name}, W={W} K={K}")
 
-    t_setup = time.perf_counter()
-    sb = StackBench(wl, W, K, agg=args.agg, scope=args.scope, kv_dtype=kv_dtype)
-    lens0, tiers, rec = sb.lens0, sb.tiers, sb.rec
-    pool_gb = 2 * L * sb.cache.k_pools[0].numel() * sb.cache.k_pools[0].element_size() / 1e9
-    log(f"set-up {time.perf_counter() - t_setup:.1f} s: {pool_gb:.1f} GB of {kv_dtype} KV pools; "
-        f"drift events at steps {sorted(sb.drift)}")
-
-    # decode-kernel bytes of one launch at step s
-    def kernel_bytes(tier, s):
-        lens = [t + s + 1 for t in lens0]
-        q_bytes = B * HQ * D * e
-        if tier == "sparse":
-            toks = sum(acc.selected_tokens(t, P, wl.k_top, wl.recency) for t in lens)
-            return toks * HKV * kv_row * 2 + q_bytes + B * HKV * (wl.k_top + wl.recency) * 4
-        return sum(lens) * HKV * kv_row * 2 + q_bytes
-
-    mid = [t + W + K // 2 + 1 for t in lens0]
-    step_bytes = acc.stack_bytes(mid, tiers, HQ, HKV, D, e, P, wl.k_top, wl.recency, kv_row)
-    present = sorted(set(tiers))
-    dom = max(present, key=lambda t: step_bytes[t])
-
-    # A: the timed DELTA stack, events around the dominant tier's decode kernel
-    trA = Tracer(torch, [dom], K * tiers.count(dom))
-    tA = sb.run(tiers, trA)
-    value = B * K / tA
-    log(f"DELTA stack: {tA / K * 1e3:.3f} ms/step, {value:.0f} tok/s")
-
-    def summarize(records):
-        out = {}
-        for s, layer, tier, (e0, e1) in records:
-            d = out.setdefault(tier, {"launches": 0, "ms": 0.0, "bytes": 0})
-            d["launches"] += 1
-            d["ms"] += event_elapsed_ms(e0, e1)
-            d["bytes"] += kernel_bytes(tier, s)
-        for tier, d in out.items():
-            d["us_per_launch"] = 1e3 * d["ms"] / d["launches"]
-            d["achieved_GBps"] = d["bytes"] / (d["ms"] * 1e-3) / 1e9
-            d["bytes_per_launch"] = d["bytes"] / d["launches"]
-            d["frac_of_peak"] = d["achieved_GBps"] / PEAK_HBM_GBPS
-        return out
-
-    domA = summarize(trA.records)[dom]
-
-    # B: per-tier breakdown (events around every decode kernel)
-    trB = Tracer(torch, present, K * L)
-    sb.run(tiers, trB)
-    per_tier = summarize(trB.records)
-    for t, d in per_tier.items():
-        d["ms_per_step"] = d["ms"] / K
-    log("tiers: " + ", ".join(f"{t} {d['us_per_launch']:.1f} us {d['achieved_GBps']:.0f} GB/s"
-                              for t, d in sorted(per_tier.items())))
-
-    # C: the same stack with every layer full, same inputs
-    tC = sb.run(["full"] * L)
-    full_value = B * K / tC
-    log(f"all-full stack: {tC / K * 1e3:.3f} ms/step, {full_value:.0f} tok/s")
-
-    attended_delta = acc.attended_tokens(mid, tiers, P, wl.k_top, wl.recency)
-    attended_full = acc.attended_tokens(mid, ["full"] * L, P, wl.k_top, wl.recency)
-    total_step_bytes = sum(step_bytes.values())
-
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            with open(TRAFFIC_FILE) as f:
-                tj = json.load(f)
-            ent = tj.get("kernels", {}).get(dom)
-            if (tj.get("source_hash") == kernel_source_hash() and tj.get("workload") == wl.name and ent
-                    and tj.get("kv_dtype", wl.dtype) == kv_dtype):
-                traffic = ent["hbm_bytes_per_launch"]
-        except (OSError, ValueError, KeyError):
-            traffic = None
-
+    head, sb = measure_stack(torch, wl, W, K, args.agg, args.scope, kv_dtype, keep=not args.no_fidelity)
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(head["tokens_per_s"], 2),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": round(tA / K * 1e3, 4),
+        "ms_per_step": round(head["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded Philox inputs generated on the device; no datasets or weights)",
-        "config": {
-            "workload": wl.name,
-            "layers": L, "batch": B, "context": wl.context, "q_heads": HQ, "kv_heads": HKV, "head_dim": D,
-            "page": P, "top_k_pages": wl.k_top, "recency_pages": wl.recency,
-            "full_layers": list(wl.full_layers), "delta_layers": list(wl.delta_layers),
-            "ragged_min": wl.ragged_min, "agg": args.agg, "scope": args.scope, "kv_dtype": kv_dtype,
-            "salient_strength": wl.salient_strength,
-            "parallelism": "single GPU",
-        },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": KERNEL_NAMES[dom].format(esz=KV_ESZ[kv_dtype]),
-            "achieved": round(domA["achieved_GBps"], 1),
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": round(domA["achieved_GBps"] / PEAK_HBM_GBPS, 4),
-            "traffic": traffic,
-            "bytes_per_launch": int(domA["bytes_per_launch"]),
-            "us_per_launch": round(domA["us_per_launch"], 2),
-            "launches": domA["launches"],
-        },
-        "tiers": {t: {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
-                  for t, d in per_tier.items()},
-        "all_full_tokens_per_s": round(full_value, 2),
-        "all_full_ms_per_step": round(tC / K * 1e3, 4),
-        "speedup_vs_all_full": round(value / full_value, 4),
-        "attended_token_ratio": round(attended_full / attended_delta, 4),
-        "algorithmic_bytes_per_step": {t: int(v) for t, v in step_bytes.items()},
-        "stack_GBps": round(total_step_bytes / (tA / K) / 1e9, 1),
-        "device": props.name,
+        "config": workload_config(wl, args.agg, args.scope, kv_dtype),
     }
+    result.update({k: v for k, v in head.items() if k not in ("tokens_per_s", "ms_per_step", "steps", "warmup")})
+    result["device"] = props.name
+
     # D: selection fidelity (untimed): at sampled steps every sparse layer is also run
-    # with full attention on the same query; recall = exp(lse_sparse - lse_full)
-    result["fidelity"] = fidelity_pass(sb, torch)
-    if result["fidelity"]:
-        log("fidelity: recall mean {recall_mean}, p05 {recall_p05}, min {recall_min}; max |out err| "
-            "{max_abs_out_err}".format(**result["fidelity"]))
-    del sb
-    torch.cuda.empty_cache()
+    # with full attention on the same query; recall = exp(lse_sparse - lse_full).  Once on
+    # the timed inputs, once with sharper attention (stronger salient keys).
+    if not args.no_fidelity:
+        fid = [dict(salient_strength=wl.salient_strength, **fidelity_pass(sb, torch))]
+        del sb
+        torch.cuda.empty_cache()
+        if args.sharp_strength and args.sharp_strength != wl.salient_strength:
+            wl_s = dataclasses.replace(wl, salient_strength=args.sharp_strength)
+            sb_s = StackBench(wl_s, W, K, agg=args.agg, scope=args.scope, kv_dtype=kv_dtype)
+            fid.append(dict(salient_strength=args.sharp_strength, **fidelity_pass(sb_s, torch)))
+            del sb_s
+            torch.cuda.empty_cache()
+        for f in fid:
+            if "recall_mean" not in f:
+                continue
+            log("fidelity at salient strength {salient_strength}: recall mean {recall_mean}, p05 {recall_p05}, "
+                "min {recall_min}; max |out err| {max_abs_out_err}".format(**f))
+        result["fidelity"] = fid
+
+    # E: the other stack workloads, each at its own step count (timed too)
+    if not args.no_workloads and not custom:
+        result["workloads"] = {}
+        for name in STACK_WORKLOADS:
+            if name == wl.name:
+                continue
+            w2 = get(name)
+            summ, _ = measure_stack(torch, w2, w2.warmup, w2.steps, args.agg, args.scope, None)
+            summ["config"] = workload_config(w2, args.agg, args.scope)
+            summ["tokens_per_s"] = round(summ["tokens_per_s"], 2)
+            summ["ms_per_step"] = round(summ["ms_per_step"], 4)
+            result["workloads"][name] = summ
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, rec, tiers, W, args.cpu_rows, kv_dtype)
+        result["cpu_baseline"] = cpu_baseline(wl, Recipe_of(wl), sb_tiers(wl), W, args.cpu_rows, kv_dtype)
     print(json.dumps(result), flush=True)
+
+
+def Recipe_of(wl):
+    from workload import Recipe
+    return Recipe(wl)
+
+
+def sb_tiers(wl):
+    from layer_aware_kv_amd import layer_tiers
+    return layer_tiers(wl.num_layers, wl.full_layers, wl.delta_layers)
 
 
 def fidelity_pass(sb, torch):
@@ -458,8 +532,20 @@ def cpu_baseline(wl, rec, tiers, step, rows, kv_dtype, repeats=3):
         "seconds_per_layer": {t: round(float(np.median(v)), 4) for t, v in times.items()},
         "oracle_seconds": round(total, 2),
         "repeats": repeats,
-        "cpu": platform.processor() or platform.machine(),
+        "cpu": cpu_model(),
     }
+
+
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), else what platform reports."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 if __name__ == "__main__":

@@ -111,8 +111,10 @@ lak_status lak_cache_destroy(lak_cache* cache);
 /* Starts a new batch of `batch` sequences with prefilled lengths host_lens[b]
  * (>= 0).  Frees every page, then gives sequence b the pages for
  * host_lens[b] + reserve_tokens tokens (reserve_tokens >= 0 pre-reserves pages for
- * later decode steps so that lak_step_begin needs no new page).  Writes the page
- * table rows and seq_lens on `stream`.  The caller then fills the cache with
+ * later decode steps so that lak_step_begin needs no new page).  Uploads the page
+ * table rows and seq_lens on `stream` from host copies that the cache keeps until
+ * the upload has completed (the next lak_seq_reset and lak_cache_destroy wait for
+ * it; the call itself does not).  The caller then fills the cache with
  * lak_kv_prefill.  Errors: EINVAL, ENOPAGE (pool too small; the cache is then left
  * with no active batch). */
 lak_status lak_seq_reset(lak_cache* cache, int32_t batch, const int32_t* host_lens,
@@ -142,7 +144,9 @@ size_t lak_workspace_bytes(const lak_cache* cache);
 
 /* Writes this step's key and value of every active sequence into layer `layer` at
  * position T_b - 1 (call after lak_step_begin).  k_new, v_new: device
- * [B][Hkv][D] in the cache dtype. */
+ * [B][Hkv][D] in the cache dtype.  DELTA keeps every token of the context in the
+ * cache ("Methodology in Plain English": no token is evicted, so memory use is that
+ * of full attention); this is how each decode step's token enters it. */
 lak_status lak_kv_append(lak_cache* cache, int32_t layer, const void* k_new, const void* v_new,
                          void* stream);
 
@@ -182,8 +186,10 @@ lak_status lak_attn_full(lak_cache* cache, int32_t layer, const void* q, const v
                          const void* v_new, float sm_scale, void* out, float* lse, void* ws,
                          size_t ws_bytes, void* stream);
 
-/* Delta-layer: the full attention of lak_attn_full (same out / lse), plus the page
- * selection it installs.  Per token t < T_b: a_t = AGG over the scope's heads of
+/* Delta-layer ("Methodology in Plain English" and "Main Findings", DELTA AI summary
+ * page: a delta-layer attends to the whole context and renews the page choice of
+ * the layers after it): the full attention of lak_attn_full (same out / lse), plus
+ * the page selection it installs.  Per token t < T_b: a_t = AGG over the scope's heads of
  * exp(logit_{h,t} - lse_h); page score S_j = sum of a_t over the valid tokens of
  * page j.  Selection per row (row = (b, kv head) for GROUP, b for ALL): the last
  * `recency` pages, plus the `k_top` older pages of largest score (ties: lower page
@@ -209,8 +215,10 @@ lak_status lak_page_select(lak_cache* cache, const float* page_scores, int32_t s
                            int32_t k_top, int32_t recency, int32_t* sel, int32_t* sel_count,
                            int32_t sel_capacity, void* stream);
 
-/* Sparse layer: attention of every query head over the tokens t < T_b of the pages
- * listed in the selection of its KV head (sel / sel_count as written by
+/* Sparse layer ("Methodology in Plain English", DELTA AI summary page: the layers
+ * after a delta-layer attend only to the tokens of the pages it chose): attention of
+ * every query head over the tokens t < T_b of the pages listed in the selection of
+ * its KV head (sel / sel_count as written by
  * lak_attn_delta_select with the same scope; entries outside [0, NP_b) are
  * skipped; duplicates are the caller's error).  The softmax is over those tokens
  * only.  A row with no valid page yields out = 0 and lse = -inf. */
@@ -227,9 +235,13 @@ lak_status lak_attn_sparse(lak_cache* cache, int32_t layer, const void* q, const
  * delta-layer before l), appending k_new[l] / v_new[l] inside the call.  All host
  * arrays have num_layers entries of device pointers; lse[l] may be NULL; sel[l] /
  * sel_count[l] are used (and required) for delta layers only, shaped as in
- * lak_attn_delta_select with sel_capacity >= k_top + recency.  Everything is
- * validated before anything is enqueued; errors: EINVAL (bad tier, a sparse layer
- * before any delta-layer, NULL pointer), plus those of lak_step_begin. */
+ * lak_attn_delta_select with sel_capacity >= k_top + recency.  Every argument is
+ * validated before anything is enqueued or any length changes; errors: EINVAL (bad
+ * tier, a sparse layer before any delta-layer, NULL pointer), plus those of
+ * lak_step_begin.  Past validation only a failing kernel launch (LAK_EHIP) can end
+ * the call early: the step has then begun (lengths advanced, page-table update
+ * enqueued) and the layers before the failing one are enqueued; such a failure
+ * means the device is unusable, not that the step can be retried. */
 typedef struct {
   int32_t num_layers;
   const int32_t* tiers;        /* host [num_layers]: 0 full, 1 delta, 2 sparse */
@@ -250,9 +262,10 @@ typedef struct {
 lak_status lak_stack_step(lak_cache* cache, const lak_stack_step_desc* step, void* ws, size_t ws_bytes,
                           void* stream);
 
-/* Tracing: while set, every attention call on `cache` records `before` and `after`
- * (hipEvent_t created by the caller) on its stream immediately before and after
- * its split-K decode kernel, so hipEventElapsedTime gives that kernel's duration.
+/* Tracing: while set, every attention call on `cache` attaches `before` and `after`
+ * (hipEvent_t created by the caller, with timing) to the dispatch of its split-K
+ * decode kernel on its stream (hipExtLaunchKernelGGL), so that they take the
+ * kernel's start and end times and hipEventElapsedTime gives its execution time.
  * NULL, NULL stops it.  Errors: EINVAL if exactly one event is NULL. */
 lak_status lak_trace_decode(lak_cache* cache, void* before, void* after);
 

@@ -110,8 +110,11 @@ struct lak_cache {
   std::vector<int32_t> lens;
   std::vector<std::vector<int32_t>> pages;
   std::vector<int32_t> free_list;  // stack; back() is handed out next
+  // host sources of lak_seq_reset's uploads: kept until `staging_done` (recorded after
+  // the copies) has completed, so that the call need not wait for them
   std::vector<int32_t> table_staging;
   std::vector<int32_t> lens_staging;
+  hipEvent_t staging_done = nullptr;
   int s_cap = 0;
   hipEvent_t trace_before = nullptr, trace_after = nullptr;
 
@@ -276,9 +279,7 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
     a.sum_pairs = (mode == MODE_DELTA && agg == LAK_AGG_SUM) ? 1 : 0;
   }
   a.t_pad = (int64_t)d.max_pages_per_seq * d.page_size;
-  if (c->trace_before) e = hipEventRecord(c->trace_before, st);
-  if (e == hipSuccess) e = launch_decode(d.dtype, mode, d.head_dim, a, splits, c->batch, st);
-  if (e == hipSuccess && c->trace_after) e = hipEventRecord(c->trace_after, st);
+  e = launch_decode(d.dtype, mode, d.head_dim, a, splits, c->batch, st, c->trace_before, c->trace_after);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
 
   CombineArgs cb;
@@ -399,6 +400,11 @@ lak_status lak_cache_create(const lak_cache_desc* desc, lak_cache** out) {
 }
 
 lak_status lak_cache_destroy(lak_cache* c) {
+  if (c && c->staging_done) {
+    // the last upload may still read the staging vectors freed with the cache
+    hipEventSynchronize(c->staging_done);
+    hipEventDestroy(c->staging_done);
+  }
   delete c;
   return ok();
 }
@@ -418,6 +424,13 @@ lak_status lak_seq_reset(lak_cache* c, int32_t batch, const int32_t* host_lens, 
       return fail(LAK_EINVAL, "sequence %d needs %lld pages > max_pages_per_seq %d", b, (long long)np,
                   c->d.max_pages_per_seq);
     need += np;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (c->staging_done) {
+    // the previous call's uploads read the staging vectors refilled below (complete
+    // long before in any real use: this returns at once)
+    hipError_t e = hipEventSynchronize(c->staging_done);
+    if (e != hipSuccess) return hip_fail(e, "previous page table upload");
   }
   c->batch = -1;
   c->reset_free_list();
@@ -439,14 +452,16 @@ lak_status lak_seq_reset(lak_cache* c, int32_t batch, const int32_t* host_lens, 
   for (int b = 0; b < batch; ++b)
     std::copy(c->pages[b].begin(), c->pages[b].end(), c->table_staging.begin() + (size_t)b * mp);
   c->lens_staging.assign(c->lens.begin(), c->lens.begin() + batch);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(c->d.page_table, c->table_staging.data(), c->table_staging.size() * 4,
-                                hipMemcpyHostToDevice, st);
+  hipError_t e = hipSuccess;
+  if (!c->staging_done) e = hipEventCreateWithFlags(&c->staging_done, hipEventDisableTiming);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(c->d.page_table, c->table_staging.data(), c->table_staging.size() * 4,
+                       hipMemcpyHostToDevice, st);
   if (e == hipSuccess)
     e = hipMemcpyAsync(c->d.seq_lens, c->lens_staging.data(), c->lens_staging.size() * 4,
                        hipMemcpyHostToDevice, st);
-  // the staging vectors must outlive the copies
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  // the staging vectors outlive the copies: the next reset and destroy wait for this
+  if (e == hipSuccess) e = hipEventRecord(c->staging_done, st);
   if (e != hipSuccess) return hip_fail(e, "page table upload");
   return ok();
 }

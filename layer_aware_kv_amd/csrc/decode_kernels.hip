@@ -19,6 +19,8 @@
 
 #include <algorithm>
 
+#include <hip/hip_ext.h>
+
 #include "lak_combine.h"
 #include "lak_device.h"
 #include "lak_internal.h"
@@ -661,19 +663,32 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
   combine_head<ESZ, D, NF>(a, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
-template <int ESZ, int D, int U>
-static void launch_decode_u(int mode, const DecodeArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  if (mode == MODE_FULL)
-    hipLaunchKernelGGL((decode_kernel<ESZ, D, MODE_FULL, U>), grid, dim3(256), lds, st, a);
-  else if (mode == MODE_DELTA)
-    hipLaunchKernelGGL((decode_kernel<ESZ, D, MODE_DELTA, U>), grid, dim3(256), lds, st, a);
+// With trace events the kernel is launched with them attached to its own dispatch
+// (hipExtLaunchKernelGGL): `ev0` / `ev1` take the kernel's start and end times, so
+// their difference is the kernel's execution, with no separate event packets around it.
+template <int ESZ, int D, int MODE, int U>
+static void launch_decode_m(const DecodeArgs& a, dim3 grid, size_t lds, hipStream_t st, hipEvent_t ev0,
+                            hipEvent_t ev1) {
+  if (ev0 && ev1)
+    hipExtLaunchKernelGGL((decode_kernel<ESZ, D, MODE, U>), grid, dim3(256), (uint32_t)lds, st, ev0, ev1, 0u, a);
   else
-    hipLaunchKernelGGL((decode_kernel<ESZ, D, MODE_SPARSE, U>), grid, dim3(256), lds, st, a);
+    hipLaunchKernelGGL((decode_kernel<ESZ, D, MODE, U>), grid, dim3(256), lds, st, a);
+}
+
+template <int ESZ, int D, int U>
+static void launch_decode_u(int mode, const DecodeArgs& a, dim3 grid, size_t lds, hipStream_t st, hipEvent_t ev0,
+                            hipEvent_t ev1) {
+  if (mode == MODE_FULL)
+    launch_decode_m<ESZ, D, MODE_FULL, U>(a, grid, lds, st, ev0, ev1);
+  else if (mode == MODE_DELTA)
+    launch_decode_m<ESZ, D, MODE_DELTA, U>(a, grid, lds, st, ev0, ev1);
+  else
+    launch_decode_m<ESZ, D, MODE_SPARSE, U>(a, grid, lds, st, ev0, ev1);
 }
 
 template <int ESZ, int D>
-static hipError_t launch_decode_t(int mode, const DecodeArgs& a, int splits, int batch,
-                                  hipStream_t st) {
+static hipError_t launch_decode_t(int mode, const DecodeArgs& a, int splits, int batch, hipStream_t st,
+                                  hipEvent_t ev0, hipEvent_t ev1) {
   const int G = a.hq / a.hkv;
   size_t lds = (size_t)(kWaves * G * D + 2 * kWaves * 16) * sizeof(float);
   if (mode == MODE_DELTA && a.lds_stage)
@@ -684,30 +699,38 @@ static hipError_t launch_decode_t(int mode, const DecodeArgs& a, int splits, int
   const int u = ESZ == 4 ? 1 : tune_decode_batch(mode);
   if constexpr (ESZ != 4) {
     if (u == 4) {
-      launch_decode_u<ESZ, D, 4>(mode, a, grid, lds, st);
+      launch_decode_u<ESZ, D, 4>(mode, a, grid, lds, st, ev0, ev1);
       return hipGetLastError();
     }
     if (u == 2) {
-      launch_decode_u<ESZ, D, 2>(mode, a, grid, lds, st);
+      launch_decode_u<ESZ, D, 2>(mode, a, grid, lds, st, ev0, ev1);
       return hipGetLastError();
     }
   }
-  launch_decode_u<ESZ, D, 1>(mode, a, grid, lds, st);
+  launch_decode_u<ESZ, D, 1>(mode, a, grid, lds, st, ev0, ev1);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(int dtype, int mode, int D, const DecodeArgs& a, int splits, int batch,
-                         hipStream_t st) {
-  if (splits == 0 || batch == 0) return hipSuccess;
+hipError_t launch_decode(int dtype, int mode, int D, const DecodeArgs& a, int splits, int batch, hipStream_t st,
+                         hipEvent_t ev0, hipEvent_t ev1) {
+  if (splits == 0 || batch == 0) {
+    // nothing to launch: the trace events still mark this point of the stream
+    hipError_t e = hipSuccess;
+    if (ev0 && ev1) {
+      e = hipEventRecord(ev0, st);
+      if (e == hipSuccess) e = hipEventRecord(ev1, st);
+    }
+    return e;
+  }
   if (dtype == 0) {
-    if (D == 128) return launch_decode_t<2, 128>(mode, a, splits, batch, st);
-    if (D == 64) return launch_decode_t<2, 64>(mode, a, splits, batch, st);
+    if (D == 128) return launch_decode_t<2, 128>(mode, a, splits, batch, st, ev0, ev1);
+    if (D == 64) return launch_decode_t<2, 64>(mode, a, splits, batch, st, ev0, ev1);
   } else if (dtype == 2) {
-    if (D == 128) return launch_decode_t<1, 128>(mode, a, splits, batch, st);
-    if (D == 64) return launch_decode_t<1, 64>(mode, a, splits, batch, st);
+    if (D == 128) return launch_decode_t<1, 128>(mode, a, splits, batch, st, ev0, ev1);
+    if (D == 64) return launch_decode_t<1, 64>(mode, a, splits, batch, st, ev0, ev1);
   } else {
-    if (D == 128) return launch_decode_t<4, 128>(mode, a, splits, batch, st);
-    if (D == 64) return launch_decode_t<4, 64>(mode, a, splits, batch, st);
+    if (D == 128) return launch_decode_t<4, 128>(mode, a, splits, batch, st, ev0, ev1);
+    if (D == 64) return launch_decode_t<4, 64>(mode, a, splits, batch, st, ev0, ev1);
   }
   return hipErrorInvalidValue;
 }

@@ -119,8 +119,9 @@ int tune_delta_lds();
 int tune_min_subtiles();
 
 // launchers (return hipSuccess or the launch error)
+// ev0 / ev1 (both or neither): events that take the decode kernel's start and end times
 hipError_t launch_decode(int dtype, int mode, int D, const DecodeArgs& a, int splits, int batch,
-                         hipStream_t st);
+                         hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_combine(int dtype, int D, const CombineArgs& a, int batch, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, int batch, hipStream_t st);
 hipError_t launch_step_update(const StepUpdate& u, int32_t* page_table, int32_t* seq_lens,
