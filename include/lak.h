@@ -14,8 +14,9 @@
  *
  * Conventions shared by every entry point
  *   - Pointers named "device" point to HIP device memory owned by the caller; the
- *     library never allocates or frees device memory.  Pointers named "host" are
- *     ordinary host memory, read before the call returns.
+ *     library never allocates or frees device memory (its only device memory of its
+ *     own is the static scratch of lak_attn_sparse_noalloc).  Pointers named "host"
+ *     are ordinary host memory, read before the call returns.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call validates
  *     its arguments on the host, enqueues its kernels on `stream` and returns
  *     without synchronising.  On a negative status nothing was enqueued and
@@ -226,6 +227,24 @@ lak_status lak_attn_sparse(lak_cache* cache, int32_t layer, const void* q, const
                            const void* v_new, float sm_scale, const int32_t* sel,
                            const int32_t* sel_count, int32_t sel_capacity, int32_t scope, void* out,
                            float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): lak_attn_sparse with the
+ * same arguments, outputs and errors, minus the workspace.  Its split partials go to
+ * a static device buffer of 16 MiB that the library owns (one copy per GPU, kept
+ * until the process ends; its address is looked up once per device, on the first
+ * call with that device current).  The call itself allocates nothing and only
+ * launches kernels.  It needs align256(B * Hq * S * D * 4) + B * Hq * S * 8 bytes of
+ * it, S = the call's splits per row (the library aims at about 1024 workgroups in
+ * all, S ~ 1024 / (B * Hkv), with at most 256 selection entries per split); a call
+ * that would need more than 16 MiB fails with LAK_EINVAL before anything is
+ * enqueued.  Every call on one GPU shares that buffer, and its
+ * kernels read only what the same call wrote: calls that may overlap on the device
+ * (different streams or threads) race and must be serialised by the caller. */
+lak_status lak_attn_sparse_noalloc(lak_cache* cache, int32_t layer, const void* q, const void* k_new,
+                                   const void* v_new, float sm_scale, const int32_t* sel,
+                                   const int32_t* sel_count, int32_t sel_capacity, int32_t scope, void* out,
+                                   float* lse, void* stream);
 
 /* One decode step of a whole attention stack (the three-tier schedule of
  * "Methodology in Plain English": full layers, delta-layers that renew the page

@@ -71,6 +71,7 @@ SIGNATURES = {
                                    _P, C.c_size_t, _P]),
     "lak_page_select": (_S, [_P, _P, _I32, _I32, _I32, _P, _P, _I32, _P]),
     "lak_attn_sparse": (_S, [_P, _I32, _P, _P, _P, _F, _P, _P, _I32, _I32, _P, _P, _P, C.c_size_t, _P]),
+    "lak_attn_sparse_noalloc": (_S, [_P, _I32, _P, _P, _P, _F, _P, _P, _I32, _I32, _P, _P, _P]),
     "lak_stack_step": (_S, [_P, C.POINTER(StackStepDesc), _P, C.c_size_t, _P]),
     "lak_trace_decode": (_S, [_P, _P, _P]),
     "lak_last_error": (C.c_char_p, []),

@@ -197,3 +197,14 @@ class PagedKVCache:
                                         _ptr(sel), _ptr(sel_count), sel.shape[-1], _SCOPE[scope], _ptr(out),
                                         _ptr(lse), _ptr(self.ws), self.ws.numel(), _stream()), "lak_attn_sparse")
         return out, lse
+
+    def attn_sparse_noalloc(self, layer, q, sm_scale, sel, sel_count, scope="group", out=None, lse=None,
+                            k_new=None, v_new=None):
+        """attn_sparse with its split partials in the library's static device scratch
+        instead of the workspace (for callers that cannot allocate; calls that overlap on
+        the device race).  ``out`` / ``lse`` must be given where the caller cannot allocate."""
+        out, lse = self._out(out, lse)
+        L.check(L.lib().lak_attn_sparse_noalloc(self._h, layer, _ptr(q), _ptr(k_new), _ptr(v_new), float(sm_scale),
+                                                _ptr(sel), _ptr(sel_count), sel.shape[-1], _SCOPE[scope], _ptr(out),
+                                                _ptr(lse), _stream()), "lak_attn_sparse_noalloc")
+        return out, lse

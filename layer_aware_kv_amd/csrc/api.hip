@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -102,6 +103,13 @@ int lak::tune_delta_lds() {
   return v;
 }
 
+// Static device scratch of lak_attn_sparse_noalloc: the split partials of one call, in
+// memory the library itself owns (one copy per GPU, held until the process ends), for
+// callers that cannot allocate.  Host code never uses this name as an address: the
+// device address of each GPU's copy comes from hipGetSymbolAddress (noalloc_scratch).
+constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
 struct lak_cache {
   lak_cache_desc d;
   std::vector<void*> kp, vp;
@@ -182,6 +190,29 @@ int plan_pps(int64_t work, int max_items, int max_splits, int subtiles_per_page,
   return std::min(std::max(std::max(pps, min_pps), 1), mode == MODE_FULL ? kMaxItemsPerSplitFull : kMaxItemsPerSplit);
 }
 
+// Device address of the current GPU's copy of `scratch`, looked up once per device
+// (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+lak_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LAK_EUNSUPPORTED, "device ordinal %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(LAK_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LAK_OK;
+}
+
 lak_status check_cache(const lak_cache* c, bool need_device) {
   if (!c) return fail(LAK_EINVAL, "cache is NULL");
   if (c->batch < 0) return fail(LAK_ESTATE, "no active batch: call lak_seq_reset first");
@@ -215,13 +246,22 @@ lak_status check_ws(const lak_cache* c, const void* ws, size_t ws_bytes) {
   return LAK_OK;
 }
 
+// Bytes of the split partials (o, then (max, sum)) of a call with `splits` splits per row.
+size_t partial_bytes(const lak_cache* c, int splits) {
+  const size_t rows = (size_t)c->batch * c->d.num_q_heads * splits;
+  return align256(rows * c->d.head_dim * sizeof(float)) + rows * 2 * sizeof(float);
+}
+
 // Runs the split-K decode plus combine of one tier.
 // With `defer_combine` the combine arguments are returned there instead of launched
-// (the delta layer combines inside its page-scoring launch).
+// (the delta layer combines inside its page-scoring launch).  With `parts` the split
+// partials go there (at most `parts_cap` bytes, checked before anything is launched)
+// instead of the workspace, which is then not used.
 lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const void* k_new,
                          const void* v_new, float sm_scale, void* out, float* lse, const int32_t* sel,
                          const int32_t* sel_count, int sel_cap, int sel_rows, void* ws, hipStream_t st,
-                         int agg = LAK_AGG_MAX, CombineArgs* defer_combine = nullptr) {
+                         int agg = LAK_AGG_MAX, CombineArgs* defer_combine = nullptr, void* parts = nullptr,
+                         size_t parts_cap = 0) {
   const auto& d = c->d;
   const WsLayout w = ws_layout(c);
   char* wsb = static_cast<char*>(ws);
@@ -241,6 +281,9 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
   const int splits = (max_items + pps - 1) / pps;
   if ((int64_t)splits * c->batch > c->s_cap)
     return fail(LAK_EINVAL, "internal: %d splits x %d rows exceed capacity %d", splits, c->batch, c->s_cap);
+  if (parts && partial_bytes(c, splits) > parts_cap)
+    return fail(LAK_EINVAL, "split partials need %zu bytes, more than the %zu-byte static scratch (batch %d, %d splits)",
+                partial_bytes(c, splits), parts_cap, c->batch, splits);
 
   DecodeArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -267,11 +310,20 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
   a.sel_count = sel_count;
   a.sel_cap = sel_cap;
   a.sel_rows = sel_rows;
-  a.o_part = reinterpret_cast<float*>(wsb + w.o_part);
-  a.ml_part = reinterpret_cast<float*>(wsb + w.ml_part);
-  a.pairs = reinterpret_cast<float*>(wsb + w.delta);
-  a.rel_w = reinterpret_cast<uint16_t*>(wsb + w.delta);
-  a.rel_max = reinterpret_cast<float*>(wsb + w.rel_max);
+  if (parts) {
+    char* pb = static_cast<char*>(parts);
+    a.o_part = reinterpret_cast<float*>(pb);
+    a.ml_part = reinterpret_cast<float*>(pb + align256((size_t)c->batch * d.num_q_heads * splits * d.head_dim *
+                                                       sizeof(float)));
+  } else {
+    a.o_part = reinterpret_cast<float*>(wsb + w.o_part);
+    a.ml_part = reinterpret_cast<float*>(wsb + w.ml_part);
+  }
+  if (mode == MODE_DELTA) {
+    a.pairs = reinterpret_cast<float*>(wsb + w.delta);
+    a.rel_w = reinterpret_cast<uint16_t*>(wsb + w.delta);
+    a.rel_max = reinterpret_cast<float*>(wsb + w.rel_max);
+  }
   {
     const int G = d.num_q_heads / d.num_kv_heads;
     const size_t staged = delta_stage_bytes(pps, d.page_size, G, agg == LAK_AGG_SUM);
@@ -684,6 +736,26 @@ lak_status lak_attn_sparse(lak_cache* c, int32_t layer, const void* q, const voi
   const int sel_rows = scope == LAK_SCOPE_GROUP ? c->d.num_kv_heads : 1;
   return run_attention(c, layer, MODE_SPARSE, q, k_new, v_new, sm_scale, out, lse, sel, sel_count, sel_capacity,
                        sel_rows, ws, static_cast<hipStream_t>(stream));
+}
+
+lak_status lak_attn_sparse_noalloc(lak_cache* c, int32_t layer, const void* q, const void* k_new,
+                                   const void* v_new, float sm_scale, const int32_t* sel, const int32_t* sel_count,
+                                   int32_t sel_capacity, int32_t scope, void* out, float* lse, void* stream) {
+  lak_status s = check_cache(c, true);
+  if (s != LAK_OK) return s;
+  if ((s = check_layer(c, layer)) != LAK_OK) return s;
+  if (c->batch == 0) return ok();
+  if (!q || !out) return fail(LAK_EINVAL, "q / out is NULL");
+  if (!sel || !sel_count) return fail(LAK_EINVAL, "sel / sel_count is NULL");
+  if (sel_capacity <= 0) return fail(LAK_EINVAL, "sel_capacity must be > 0");
+  if (scope != LAK_SCOPE_GROUP && scope != LAK_SCOPE_ALL) return fail(LAK_EINVAL, "bad scope %d", scope);
+  if ((k_new == nullptr) != (v_new == nullptr)) return fail(LAK_EINVAL, "give both k_new and v_new or neither");
+  void* parts = nullptr;
+  if ((s = noalloc_scratch(&parts)) != LAK_OK) return s;
+  const int sel_rows = scope == LAK_SCOPE_GROUP ? c->d.num_kv_heads : 1;
+  return run_attention(c, layer, MODE_SPARSE, q, k_new, v_new, sm_scale, out, lse, sel, sel_count, sel_capacity,
+                       sel_rows, nullptr, static_cast<hipStream_t>(stream), LAK_AGG_MAX, nullptr, parts,
+                       kNoallocScratchBytes);
 }
 
 lak_status lak_stack_step(lak_cache* c, const lak_stack_step_desc* st, void* ws, size_t ws_bytes, void* stream) {
