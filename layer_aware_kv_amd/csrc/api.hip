@@ -98,6 +98,13 @@ int lak::tune_min_subtiles() {
   return v;
 }
 
+int lak::tune_topk_wave_kpl() {
+  // 0 by default: the workgroup selector measured faster at every row length tried
+  // (512 to 8000 pages, 16 x 4 rows: 7.6-17 us against 9.0-42.6 us for one wave per row)
+  static const int v = env_int("LAK_TUNE_TOPK_WAVE_KPL", 0, 0, 128);
+  return v;
+}
+
 int lak::tune_delta_lds() {
   static const int v = env_int("LAK_TUNE_DELTA_LDS", 1, 0, 1);
   return v;
@@ -147,7 +154,7 @@ struct lak_cache {
 namespace {
 
 struct WsLayout {
-  size_t o_part, ml_part, delta, rel_max, scores, total;
+  size_t o_part, ml_part, delta, scores, total;
 };
 
 WsLayout ws_layout(const lak_cache* c) {
@@ -160,16 +167,14 @@ WsLayout ws_layout(const lak_cache* c) {
   off = align256(off + part * d.head_dim * sizeof(float));
   w.ml_part = off;
   off = align256(off + part * 2 * sizeof(float));
-  // delta scratch: fp16 relative weights [B][Hkv][sub-tiles][Gp][16] (MAX) or the
-  // (max, sum) pairs [B][Hkv][sub-tiles][Gp][2] float (SUM), then the sub-tile maxima
-  // [B][Hkv][sub-tiles][Gp] float (MAX); Gp = G rounded up to even
+  // delta scratch, per (b, g, 16-token sub-tile) of the cache's capacity: the MAX block
+  // (G x 16 fp16 relative weights, then G float maxima, max_block_bytes(G) bytes) or the
+  // SUM (max, sum) float pairs of Gp heads (Gp = G rounded up to even)
   w.delta = off;
   const int G = d.num_q_heads / d.num_kv_heads;
   const size_t gp = (size_t)(G + (G & 1));
-  const size_t blocks = (size_t)d.max_batch * d.num_kv_heads * gp * ((size_t)d.max_pages_per_seq * d.page_size / 16);
-  off = align256(off + blocks * 16 * 2);
-  w.rel_max = off;
-  off = align256(off + blocks * sizeof(float));
+  const size_t subs = (size_t)d.max_batch * d.num_kv_heads * ((size_t)d.max_pages_per_seq * d.page_size / 16);
+  off = align256(off + subs * std::max((size_t)max_block_bytes(G), gp * 2 * sizeof(float)));
   w.scores = off;
   off = align256(off + (size_t)d.max_batch * d.num_kv_heads * d.max_pages_per_seq * sizeof(float));
   w.total = off;
@@ -212,6 +217,37 @@ lak_status noalloc_scratch(void** out) {
   *out = g_scratch_ptr[dev];
   return LAK_OK;
 }
+
+#ifdef LAK_DEBUG_CHECKS
+// Debug builds: after every allocation, every page id held by an active sequence is a
+// valid physical page (< num_pages), no page is held twice or also free, and held plus
+// free pages make up the pool.  A violation is a library bug: report and abort.
+void debug_check_pages(const lak_cache* c) {
+  const int64_t n = c->d.num_pages;
+  std::vector<uint8_t> seen((size_t)n, 0);
+  int64_t held = 0;
+  auto bad = [&](const char* what, long long v) {
+    std::fprintf(stderr, "lak debug check: %s (%lld)\n", what, v);
+    std::abort();
+  };
+  for (int b = 0; b < std::max(c->batch, 0); ++b) {
+    if ((int64_t)c->pages[b].size() * c->d.page_size < c->lens[b]) bad("sequence shorter in pages than its length", b);
+    for (int32_t p : c->pages[b]) {
+      if (p < 0 || p >= n) bad("page id outside the pool", p);
+      if (seen[(size_t)p]++) bad("page held twice", p);
+      ++held;
+    }
+  }
+  for (int32_t p : c->free_list) {
+    if (p < 0 || p >= n) bad("free page id outside the pool", p);
+    if (seen[(size_t)p]++) bad("page both free and held", p);
+  }
+  if (held + (int64_t)c->free_list.size() != n) bad("pages lost", n - held - (int64_t)c->free_list.size());
+}
+#define LAK_DEBUG_CHECK_PAGES(c) debug_check_pages(c)
+#else
+#define LAK_DEBUG_CHECK_PAGES(c) ((void)0)
+#endif
 
 lak_status check_cache(const lak_cache* c, bool need_device) {
   if (!c) return fail(LAK_EINVAL, "cache is NULL");
@@ -321,8 +357,7 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
   }
   if (mode == MODE_DELTA) {
     a.pairs = reinterpret_cast<float*>(wsb + w.delta);
-    a.rel_w = reinterpret_cast<uint16_t*>(wsb + w.delta);
-    a.rel_max = reinterpret_cast<float*>(wsb + w.rel_max);
+    a.rel_blk = reinterpret_cast<uint8_t*>(wsb + w.delta);
   }
   {
     const int G = d.num_q_heads / d.num_kv_heads;
@@ -372,6 +407,7 @@ lak_status run_select(lak_cache* c, const float* scores, int scope, int k_top, i
   t.k_top = k_top;
   t.recency = recency;
   t.sel_cap = sel_cap;
+  t.max_np = c->max_np();
   hipError_t e = launch_topk(t, c->batch, st);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return ok();
@@ -454,8 +490,8 @@ lak_status lak_cache_create(const lak_cache_desc* desc, lak_cache** out) {
 lak_status lak_cache_destroy(lak_cache* c) {
   if (c && c->staging_done) {
     // the last upload may still read the staging vectors freed with the cache
-    hipEventSynchronize(c->staging_done);
-    hipEventDestroy(c->staging_done);
+    (void)hipEventSynchronize(c->staging_done);
+    (void)hipEventDestroy(c->staging_done);
   }
   delete c;
   return ok();
@@ -498,6 +534,7 @@ lak_status lak_seq_reset(lak_cache* c, int32_t batch, const int32_t* host_lens, 
     c->lens[b] = host_lens[b];
   }
   c->batch = batch;
+  LAK_DEBUG_CHECK_PAGES(c);
   if (c->host_only || batch == 0) return ok();
   const int mp = c->d.max_pages_per_seq;
   c->table_staging.assign((size_t)batch * mp, 0);
@@ -543,6 +580,7 @@ lak_status lak_step_begin(lak_cache* c, void* stream) {
     c->pages[b].push_back(p);
   }
   for (int b = 0; b < c->batch; ++b) c->lens[b] += 1;
+  LAK_DEBUG_CHECK_PAGES(c);
   if (c->host_only) return ok();
   hipStream_t st = static_cast<hipStream_t>(stream);
   size_t i = 0;
@@ -692,8 +730,7 @@ lak_status lak_attn_delta_select(lak_cache* c, int32_t layer, const void* q, con
   char* wsb = static_cast<char*>(ws);
   float* scores = page_scores ? page_scores : reinterpret_cast<float*>(wsb + w.scores);
   pa.pairs = reinterpret_cast<const float*>(wsb + w.delta);
-  pa.rel_w = reinterpret_cast<const uint16_t*>(wsb + w.delta);
-  pa.rel_max = reinterpret_cast<const float*>(wsb + w.rel_max);
+  pa.rel_blk = reinterpret_cast<const uint8_t*>(wsb + w.delta);
   pa.seq_lens = c->d.seq_lens;
   pa.scores = scores;
   pa.t_pad = (int64_t)c->d.max_pages_per_seq * c->d.page_size;

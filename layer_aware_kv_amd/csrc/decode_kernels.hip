@@ -310,40 +310,49 @@ __global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) v
     n_items = min(max(a.sel_count[row], 0), min(a.sel_cap, NP));
     sel_row = a.sel + row * a.sel_cap;
   }
-  // Fused append: split 0 of each (b, g) writes this step's token at T-1 into the
-  // pool for later calls; the wave that attends over that sub-tile in this call
-  // stores the same bytes itself before its loads (below), or, on the delta tier of
-  // bfloat16 / fp32 pools, patches the token into its fragments (`patch`).
+  // Fused append.  The wave whose items include the page of this step's token (T-1)
+  // stores that row into the pool itself before its loads (below) -- or, on the delta
+  // tier of bfloat16 / fp32 pools, patches it into its fragments (`patch`).  On the full
+  // tier (and the fp8 delta tier) that wave always exists, since every page is an item,
+  // and its store is the append.  Where it may not store (delta patch; a sparse
+  // selection without the token's page), split 0 of the row also writes the row, at the
+  // end of the kernel: nothing in this call reads it from the pool but that wave, so the
+  // store does not delay the split's own loads.  Both write the same bytes.
   // (fp8 pools: rows arrive as bfloat16 and are encoded with their row scale.)
   const QE* krow_new = nullptr;
   const QE* vrow_new = nullptr;
   if (a.k_new != nullptr && T > 0) {
     krow_new = reinterpret_cast<const QE*>(a.k_new) + ((int64_t)b * a.hkv + g) * D;
     vrow_new = reinterpret_cast<const QE*>(a.v_new) + ((int64_t)b * a.hkv + g) * D;
-    if (s == 0) {
-      const int t = T - 1;
-      const int64_t phys = a.page_table[(int64_t)b * a.max_pages + t / P];
-      const int64_t row0 = (phys * a.hkv + g) * P + ((t % P) / kSub) * kSub;  // sub-tile's first row
-      E* kp = const_cast<E*>(reinterpret_cast<const E*>(a.k_pool));
-      E* vp = const_cast<E*>(reinterpret_cast<const E*>(a.v_pool));
-      if constexpr (ESZ == 1) {
-        if (threadIdx.x < 64)
-          encode_rows_fp8(D, kp + row0 * D, vp + row0 * D, t % kSub, const_cast<float*>(a.k_scale) + row0 + t % kSub,
-                          const_cast<float*>(a.v_scale) + row0 + t % kSub, krow_new, vrow_new, threadIdx.x);
-      } else {
-        for (int d = threadIdx.x; d < D; d += blockDim.x) {
-          kp[row0 * D + k_off<ESZ>(t % kSub, d)] = krow_new[d];
-          vp[row0 * D + v_off<ESZ>(t % kSub, d)] = vrow_new[d];
-        }
+  }
+  constexpr bool kOwnerStores = (ESZ == 1 || MODE != MODE_DELTA);
+  const bool split0_store = krow_new != nullptr && s == 0 && (MODE == MODE_SPARSE || !kOwnerStores);
+  auto store_token = [&]() {
+    const int t = T - 1;
+    const int64_t phys = a.page_table[(int64_t)b * a.max_pages + t / P];
+    const int64_t row0 = (phys * a.hkv + g) * P + ((t % P) / kSub) * kSub;  // sub-tile's first row
+    E* kp = const_cast<E*>(reinterpret_cast<const E*>(a.k_pool));
+    E* vp = const_cast<E*>(reinterpret_cast<const E*>(a.v_pool));
+    if constexpr (ESZ == 1) {
+      if (threadIdx.x < 64)
+        encode_rows_fp8(D, kp + row0 * D, vp + row0 * D, t % kSub, const_cast<float*>(a.k_scale) + row0 + t % kSub,
+                        const_cast<float*>(a.v_scale) + row0 + t % kSub, krow_new, vrow_new, threadIdx.x);
+    } else {
+      for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        kp[row0 * D + k_off<ESZ>(t % kSub, d)] = krow_new[d];
+        vp[row0 * D + v_off<ESZ>(t % kSub, d)] = vrow_new[d];
       }
     }
-  }
+  };
 
   // The row's items are dealt round-robin to its S_row splits (split s takes items
   // s, s + S_row, s + 2 S_row, ...): the workgroups of a row then stream neighbouring
   // pages at the same time, which keeps concurrent DRAM accesses close together.
   const int S_row = (n_items + a.pps - 1) / a.pps;
-  if (s >= S_row) return;
+  if (s >= S_row) {
+    if (split0_store) store_token();  // a row with no items (empty selection)
+    return;
+  }
   const int n_split = (n_items - s + S_row - 1) / S_row;  // items of this split
 
   // wave index made wave-uniform so that all per-sub-tile bookkeeping is scalar
@@ -397,13 +406,14 @@ __global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) v
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   // The wave whose items include the page of this step's token stores that row itself
-  // (the same bytes split 0 writes; fp8 pools: encoded) before any of its loads, so it
-  // then reads the token from the pool like any other; the workgroup-scope fence orders
-  // its lanes' stores before those loads.  This keeps the sub-tile loop free of the
-  // register patch, whose extra loads force conservative wait counts on every sub-tile
-  // (full tier 332 -> 324 us at B 16, T 64k); the delta tier of bfloat16 / fp32 pools
-  // keeps the patch, which measured faster there (372 vs 381 us).
-  if constexpr (ESZ == 1 || MODE != MODE_DELTA) {
+  // (fp8 pools: encoded) before any of its loads, so it then reads the token from the
+  // pool like any other; a workgroup-scope fence, just before it loads the token's
+  // sub-tile (x_tok), orders its lanes' stores before that load.  This keeps the
+  // sub-tile loop free of the register patch, whose extra loads force conservative
+  // wait counts on every sub-tile (full tier 332 -> 324 us at B 16, T 64k); the delta
+  // tier of bfloat16 / fp32 pools keeps the patch, which measured faster there.
+  int x_tok = -1;
+  if constexpr (kOwnerStores) {
     if (krow_new != nullptr) {
       unsigned long long own = 0ull;
       int k_own = 0;
@@ -430,8 +440,7 @@ __global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) v
             const_cast<E*>(vpool)[row0 * D + v_off<ESZ>(tt, d)] = vrow_new[d];
           }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        x_tok = k_own * spp + tin / kSub;
       }
     }
   }
@@ -455,8 +464,8 @@ __global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) v
     return Sub{valid, t0};
   };
 
-  // delta tier, LDS staging: fp16 blocks of the split's sub-tiles, then their maxima
-  const int lds_r_off = (a.pps * spp * Gp * kSub) / 2;  // in floats (2 fp16 per float)
+  // delta tier, MAX: bytes of one sub-tile's block (weights [G][16] fp16, then G maxima)
+  const int blk_bytes = max_block_bytes(G);
 
   float m2 = -INFINITY;  // running max, log2 units
   float l = 0.f;         // this lane's share of the running sum
@@ -514,33 +523,32 @@ __global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) v
           *reinterpret_cast<f32x2*>(a.pairs + (blk * Gp + n) * 2) = (f32x2){mx, e};
         }
       }
-    } else if (MODE == MODE_DELTA && n < Gp) {
+    } else if (MODE == MODE_DELTA && head_ok) {
       // MAX aggregation: this head's max logit r over the sub-tile (log2 units, exact)
       // and each token's weight relative to it, u = 2^(logit - r) in (0, 1], rounded to
       // fp16; the page score later is sum_t max_h u * 2^(r - lse_h), so its relative
-      // error is at most 2^-11.  Blocks are [Gp heads][16 tokens] (Gp = G rounded up to
-      // even, so one block is whole 64-byte lines); the padding head writes zeros.
+      // error is at most 2^-11.  One block per sub-tile: [G heads][16 tokens] weights,
+      // then the G maxima (only the group's real heads: no padding head is written).
       uint32_t hw[2];
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        const float u0 = !head_ok ? 0.f : (rel_from_p ? p[2 * r] * to_rel : exp2f(s2[2 * r] - mx));
-        const float u1 = !head_ok ? 0.f : (rel_from_p ? p[2 * r + 1] * to_rel : exp2f(s2[2 * r + 1] - mx));
+        const float u0 = rel_from_p ? p[2 * r] * to_rel : exp2f(s2[2 * r] - mx);
+        const float u1 = rel_from_p ? p[2 * r + 1] * to_rel : exp2f(s2[2 * r + 1] - mx);
         hw[r] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)u0) |
                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)u1) << 16);
       }
-      const float rmax = head_ok ? mx : 0.f;
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      uint8_t* dst;
       if (a.lds_stage) {
         // staged in LDS at the sub-tile's index within the workgroup; flushed at the end
         const int li = (wave + kWaves * (x / spp)) * spp + (x % spp);
-        uint16_t* lu = reinterpret_cast<uint16_t*>(lds);
-        *reinterpret_cast<u32x2*>(lu + (li * Gp + n) * kSub + 4 * j) = (u32x2){hw[0], hw[1]};
-        if (j == 0) lds[lds_r_off + li * Gp + n] = rmax;
+        dst = reinterpret_cast<uint8_t*>(lds) + (size_t)li * blk_bytes;
       } else {
         const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + ct / kSub;
-        *reinterpret_cast<u32x2*>(a.rel_w + (blk * Gp + n) * kSub + 4 * j) = (u32x2){hw[0], hw[1]};
-        if (j == 0) a.rel_max[blk * Gp + n] = rmax;
+        dst = a.rel_blk + blk * blk_bytes;
       }
+      *reinterpret_cast<u32x2*>(dst + n * (kSub * 2) + 8 * j) = (u32x2){hw[0], hw[1]};
+      if (j == 0) *reinterpret_cast<float*>(dst + G * (kSub * 2) + 4 * n) = mx;
     }
     l = l * alpha + ps;
     m2 = m_new;
@@ -556,6 +564,10 @@ __global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) v
   // the next sub-tile's loads in flight during the math measured slower: it costs
   // occupancy, and occupancy hides the latency better.)
   for (int x = 0; x < nsub; x += U) {
+    if (kOwnerStores && x_tok >= x && x_tok < x + U) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
     F buf[U];
     Sub info[U];
 #pragma unroll
@@ -569,30 +581,19 @@ __global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) v
   }
 
   if (MODE == MODE_DELTA && a.lds_stage && !a.sum_pairs) {
-    // write the workgroup's blocks in one burst: 16-byte units of fp16 weights (two per
-    // head row), then the maxima
+    // write the workgroup's blocks in one burst, 16 bytes per thread: each block is
+    // contiguous (its tail past the maxima, if any, is padding and never read)
     __syncthreads();
     const int n_sub = n_split * spp;
-    const int n_units = n_sub * Gp * 2;
-    for (int idx = threadIdx.x; idx < n_units; idx += blockDim.x) {
-      const int half = idx & 1;
-      const int hn = (idx >> 1) % Gp;
-      const int li = (idx >> 1) / Gp;
+    const int upb = blk_bytes / 16;  // 16-byte units per block
+    for (int idx = threadIdx.x; idx < n_sub * upb; idx += blockDim.x) {
+      const int li = idx / upb, u = idx - li * upb;
       const int member = li / spp, sub = li - member * spp;
       const int t0 = (s + S_row * member) * P + sub * kSub;
       if (t0 < T) {
         const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + t0 / kSub;
-        *reinterpret_cast<u32x4*>(a.rel_w + (blk * Gp + hn) * kSub + 8 * half) =
-            *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(lds) + (li * Gp + hn) * kSub + 8 * half);
-      }
-    }
-    for (int idx = threadIdx.x; idx < n_sub * Gp; idx += blockDim.x) {
-      const int hn = idx % Gp, li = idx / Gp;
-      const int member = li / spp, sub = li - member * spp;
-      const int t0 = (s + S_row * member) * P + sub * kSub;
-      if (t0 < T) {
-        const int64_t blk = ((int64_t)b * a.hkv + g) * (a.t_pad / kSub) + t0 / kSub;
-        a.rel_max[blk * Gp + hn] = lds[lds_r_off + idx];
+        *reinterpret_cast<u32x4*>(a.rel_blk + blk * blk_bytes + 16 * u) =
+            *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(lds) + (size_t)li * blk_bytes + 16 * u);
       }
     }
     __syncthreads();  // the merge below reuses this LDS
@@ -655,6 +656,7 @@ __global__ __launch_bounds__(256, (U == 1 && ESZ != 4 ? 4 : (U <= 2 ? 3 : 2))) v
     *reinterpret_cast<f32x4*>(a.o_part + row * D + d) = acc;
     if (d == 0) *reinterpret_cast<f32x2*>(a.ml_part + row * 2) = (f32x2){M, L};
   }
+  if (split0_store) store_token();
 }
 
 // One wave per (head, sequence); NF: splits loaded in one round (0: the looped path).

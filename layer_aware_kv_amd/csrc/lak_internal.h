@@ -31,10 +31,11 @@ struct DecodeArgs {
   // outputs
   float* o_part;               // [B][Hq][s_cap][D]
   float* ml_part;              // [B][Hq][s_cap][2]  (max in log2 units, sum)
-  // delta tier, MAX aggregation: per (b, g, 16-token sub-tile, head) the head's max logit r
-  // over the sub-tile (log2 units) and every token's relative weight 2^(logit - r) in fp16:
-  uint16_t* rel_w;             // [B][Hkv][t_pad/16][Gp][16] fp16 (Gp = G rounded up to even)
-  float* rel_max;              // [B][Hkv][t_pad/16][Gp]
+  // delta tier, MAX aggregation: per (b, g, 16-token sub-tile) one block of
+  // max_block_bytes(G) bytes: every token's weight relative to the head's sub-tile max r,
+  // 2^(logit - r), in fp16 as [G heads][16 tokens], then the G maxima r (float32, log2
+  // units); blocks are [B][Hkv][t_pad/16]
+  uint8_t* rel_blk;
   int lds_stage;               // delta tier: stage the scratch in LDS, write it at the split's end
   float* pairs;                // delta tier, SUM aggregation: per (head, sub-tile) the pair
   int sum_pairs;               // (max logit in log2 units, sum of 2^(logit - max)) [..][Gp][2]
@@ -54,8 +55,8 @@ struct CombineArgs {
 };
 
 struct PageScoreArgs {
-  const uint16_t* rel_w;      // MAX: relative weights and sub-tile maxima as the decode kernel
-  const float* rel_max;       //      wrote them (DecodeArgs::rel_w, rel_max)
+  const uint8_t* rel_blk;     // MAX: the blocks of relative weights and sub-tile maxima as the
+                              //      decode kernel wrote them (DecodeArgs::rel_blk)
   const float* pairs;         // SUM: (max, sum) pairs
   CombineArgs cb;             // the delta decode's split partials: each head's LSE is merged
                               // from them, and extra blocks write the layer's out / lse
@@ -80,6 +81,7 @@ struct TopkArgs {
   int32_t* sel_count;         // [B][R]
   int rows_per_seq;           // R
   int page, max_pages, k_top, recency, sel_cap;
+  int max_np;                 // most pages of any row in the call (host lengths): picks the kernel
 };
 
 constexpr int kStepMax = 96;
@@ -105,15 +107,22 @@ struct KvGeom {
 //   LAK_TUNE_RAGGED_WGS    workgroups a full / delta launch over a ragged batch aims for (3072)
 //   LAK_TUNE_DELTA_LDS     1 (default): delta scratch staged in LDS, written at a split's end
 //   LAK_TUNE_MIN_SUBTILES  fewest 16-token sub-tiles a split-K workgroup is given (default 8)
+//   LAK_TUNE_TOPK_WAVE_KPL  largest candidate row (in 64-page units) that the one-wave
+//                          selector takes (0, the default: the workgroup selector always)
 int tune_decode_batch(int mode);
 
-// LDS bytes of a delta split's staged blocks: MAX, fp16 weights + float maxima per
-// (head, sub-tile); SUM, the (max, sum) pair.
+// Bytes of one sub-tile's MAX block: G heads x 16 fp16 weights, then G float maxima,
+// rounded up to whole 32-byte units (G = 7: 252 -> 256).
+__host__ __device__ inline int max_block_bytes(int G) { return (G * (16 * 2 + 4) + 31) & ~31; }
+
+// LDS bytes of a delta split's staged blocks: MAX, one block per sub-tile; SUM, the
+// (max, sum) pair per (head, sub-tile), Gp = G rounded up to even heads.
 inline size_t delta_stage_bytes(int pps, int page, int G, bool sum = false) {
   const size_t gp = (size_t)(G + (G & 1));
-  return (size_t)pps * (page / 16) * gp * (sum ? 2 * 4 : 16 * 2 + 4);
+  return (size_t)pps * (page / 16) * (sum ? gp * 2 * 4 : (size_t)max_block_bytes(G));
 }
 int tune_target_wgs(int mode);
+int tune_topk_wave_kpl();
 int tune_ragged_wgs();
 int tune_delta_lds();
 int tune_min_subtiles();

@@ -134,9 +134,12 @@ def _tie_scores(rng, B, R, NP, levels):
     return (rng.integers(0, levels, size=(B, R, NP)) / levels).astype(np.float32)
 
 
+# rows up to 8192 pages take the one-wave selector (16, 32, 64 or 128 keys per lane),
+# longer ones the workgroup selector (keys staged in LDS up to 12288 pages, else global)
 @pytest.mark.parametrize("NP,k_top,rec,levels", [
     (64, 8, 4, 5), (512, 96, 32, 3), (4100, 192, 64, 50), (1000, 0, 8, 4), (30, 40, 4, 3),
-    (7, 3, 9, 2), (2049, 2048, 0, 2), (300, 17, 0, 1000000), (13000, 500, 16, 7)])
+    (7, 3, 9, 2), (2049, 2048, 0, 2), (300, 17, 0, 1000000), (13000, 500, 16, 7), (1500, 100, 10, 3),
+    (3000, 250, 40, 1000000), (8192, 700, 64, 11), (8193, 300, 20, 9)])
 def test_page_select_on_oracle_scores_is_exact(NP, k_top, rec, levels):
     from layer_aware_kv_amd import PagedKVCache
     B, R, P = 3, 2, 16
