@@ -166,6 +166,36 @@ def test_page_select_on_oracle_scores_is_exact(NP, k_top, rec, levels):
             assert (sel[b, r, n:] == -1).all()
 
 
+def test_page_select_special_values():
+    """Scores that are NaN, negative, -0 or -inf order as 0; +inf is the largest; ties among
+    them (and with real zeros) go to the lower page index."""
+    from layer_aware_kv_amd import PagedKVCache
+    B, R, P, NP = 2, 2, 16, 700
+    rng = np.random.default_rng(5)
+    S = rng.random((B, R, NP)).astype(np.float32) * 1e-3
+    S[:, :, rng.choice(NP, 200, replace=False)] = 0.0
+    S[0, 0, rng.choice(NP, 60, replace=False)] = np.nan
+    S[0, 1, rng.choice(NP, 60, replace=False)] = -1.0
+    S[1, 0, rng.choice(NP, 40, replace=False)] = -np.inf
+    S[1, 0, rng.choice(NP, 5, replace=False)] = np.inf
+    S[1, 1, rng.choice(NP, 50, replace=False)] = -0.0
+    cache = PagedKVCache(1, B, 2 * R, R, 64, P, NP + 1, B * (NP + 1), "bf16")
+    cache.seq_reset([NP * P] * B)
+    dev = torch.zeros((B, R, NP + 1), dtype=torch.float32, device="cuda")
+    dev[:, :, :NP] = torch.from_numpy(S).cuda()
+    for k_top, rec in [(300, 10), (600, 20), (5, 0)]:
+        sel, cnt = cache.page_select(dev, k_top, rec)
+        torch.cuda.synchronize()
+        for b in range(B):
+            for r in range(R):
+                row = [float(x) if (x > 0) else 0.0 for x in S[b, r]]  # NaN > 0 is False
+                NC = NP - rec
+                order = sorted(range(NC), key=lambda j: (-row[j], j))[:k_top]
+                ref = sorted(order + list(range(NC, NP)))
+                n = int(cnt[b, r])
+                assert n == len(ref) and sel[b, r, :n].cpu().tolist() == ref, (b, r, k_top, rec)
+
+
 @pytest.mark.parametrize("dtype,D,P", [("bf16", 128, 16), ("f32", 64, 16), ("bf16", 128, 32), ("bf16", 64, 64)])
 def test_kv_prefill_append_gather_roundtrip(dtype, D, P):
     lens = [1, 17, 63, 200]

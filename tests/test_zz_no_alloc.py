@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_util import TOL, LSE_TOL, assert_close, fill_and_step, host, make_cache
+from tests.gpu_util import TOL, LSE_TOL, assert_close, fill_and_step, host, make_cache, to_dev
 from workload.cases import random_case, plant_salient
 
 pytestmark = pytest.mark.gpu
@@ -63,3 +63,37 @@ def test_noalloc_sparse_rejects_calls_beyond_its_scratch():
         cache.attn_sparse_noalloc(0, q, 0.1, sel, cnt, out=out, lse=lse)
     torch.cuda.synchronize()
     assert (out == 3.0).all() and (lse == 3.0).all()  # nothing was enqueued
+
+
+@pytest.mark.parametrize("kv", ["fp8", "f32"])
+def test_noalloc_sparse_other_pool_types(kv):
+    """The same comparison on fp8 (E4M3 codes + row scales) and float32 pools."""
+    from layer_aware_kv_amd import PagedKVCache
+    from oracle import quant as Q
+    act = "bf16" if kv == "fp8" else kv
+    B, HQ, HKV, D, P = 3, 16, 2, 128, 16
+    lens = [700, 33, 1500]
+    print(f"noalloc case kv={kv} lens={lens}", flush=True)
+    case = random_case(77, B, HQ, HKV, D, lens, act)
+    cache = PagedKVCache(1, B, HQ, HKV, D, P, 100, 3 * 100, kv)
+    cache.seq_reset([n - 1 for n in lens])
+    k, v = to_dev(case.K, act), to_dev(case.V, act)
+    cache.kv_prefill(0, k, v)
+    cache.step_begin()
+    kn = torch.stack([k[b, :, lens[b] - 1] for b in range(B)]).contiguous()
+    vn = torch.stack([v[b, :, lens[b] - 1] for b in range(B)]).contiguous()
+    cache.kv_append(0, kn, vn)
+    q = to_dev(case.q, act)
+    sm = float(1.0 / np.sqrt(D))
+    _, _, sel, cnt = cache.attn_delta_select(0, q, sm, 20, 3)
+    out_ws, lse_ws = cache.attn_sparse(0, q, sm, sel, cnt)
+    out_na, lse_na = cache.attn_sparse_noalloc(0, q, sm, sel, cnt)
+    torch.cuda.synchronize()
+    assert torch.equal(out_na, out_ws) and torch.equal(lse_na, lse_ws)
+    for b, T in enumerate(lens):
+        K, V = case.K[b, :, :T], case.V[b, :, :T]
+        if kv == "fp8":
+            K, V = Q.quantize_dequantize(K), Q.quantize_dequantize(V)
+        sels = [sel[b, g, :int(cnt[b, g])].cpu().tolist() for g in range(HKV)]
+        ref, _ = oracle.sparse_attention(case.q[b], K, V, sels, P, sm)
+        assert_close(host(out_na[b]), ref, TOL["f32" if kv == "f32" else "bf16"], f"noalloc {kv} b={b}")
