@@ -137,6 +137,11 @@ def test_attention_calls_on_metadata_only_cache_fail_cleanly():
     assert lib.lak_attn_full(None, 0, dummy, None, None, 1.0, dummy, None, dummy, 1 << 20, None) == L.LAK_EINVAL
     assert lib.lak_workspace_bytes(h) > 0
     assert lib.lak_stack_step(h, None, dummy, 1 << 20, None) == L.LAK_ESTATE
+    # the no-allocation variant validates like the workspace call (before any device lookup)
+    assert lib.lak_attn_sparse_noalloc(h, 0, dummy, None, None, 1.0, dummy, dummy, 4, 0, dummy, None,
+                                       None) == L.LAK_ESTATE
+    assert lib.lak_attn_sparse_noalloc(None, 0, dummy, None, None, 1.0, dummy, dummy, 4, 0, dummy, None,
+                                       None) == L.LAK_EINVAL
     lib.lak_cache_destroy(h)
 
 
@@ -144,10 +149,12 @@ def test_workspace_covers_logits_and_partials():
     lib = L.lib()
     st, h = _create(max_batch=4, max_pages=16, page=16, hq=8, hkv=2, d=64)
     ws = lib.lak_workspace_bytes(h)
-    # delta scratch per (b, kv head, 16-token sub-tile, head of the group): 16 fp16 weights
-    # and one float maximum; plus the (max, sum) split partials [Hq][s_cap][2]
-    blocks = 4 * 2 * 4 * (16 * 16 // 16)
-    assert ws >= blocks * (16 * 2 + 4) + 8 * 2 * 4
+    # delta scratch per (b, kv head, 16-token sub-tile): one block of G x 16 fp16 weights
+    # and G float maxima (G = 4: 144 bytes, padded to 160); plus the (max, sum) split
+    # partials [Hq][s_cap][2]
+    subtiles = 4 * 2 * (16 * 16 // 16)
+    assert ws >= subtiles * 4 * (16 * 2 + 4) + 8 * 2 * 4
+    assert ws >= subtiles * 160
     lib.lak_cache_destroy(h)
 
 
