@@ -285,6 +285,8 @@ lak_status lak_stack_step(lak_cache* cache, const lak_stack_step_desc* step, voi
  * (hipEvent_t created by the caller, with timing) to the dispatch of its split-K
  * decode kernel on its stream (hipExtLaunchKernelGGL), so that they take the
  * kernel's start and end times and hipEventElapsedTime gives its execution time.
+ * Events created with hipEventDisableSystemFence (read only after a device
+ * synchronisation) add the least to the stream's time.
  * NULL, NULL stops it.  Errors: EINVAL if exactly one event is NULL. */
 lak_status lak_trace_decode(lak_cache* cache, void* before, void* after);
 

@@ -96,21 +96,52 @@ def lib():
 
 
 _hip = None
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+def _hip_lib():
+    global _hip
+    if _hip is None:
+        h = C.CDLL("libamdhip64.so")
+        h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        h.hipEventElapsedTime.restype = C.c_int
+        h.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+        h.hipEventCreateWithFlags.restype = C.c_int
+        h.hipEventDestroy.argtypes = [C.c_void_p]
+        h.hipEventDestroy.restype = C.c_int
+        _hip = h
+    return _hip
 
 
 def event_elapsed_ms(before, after) -> float:
-    """hipEventElapsedTime of two completed events (torch.cuda.Event objects recorded
-    by the library, which torch itself does not know were recorded)."""
-    global _hip
-    if _hip is None:
-        _hip = C.CDLL("libamdhip64.so")
-        _hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
-        _hip.hipEventElapsedTime.restype = C.c_int
+    """hipEventElapsedTime of two completed events (TimingEvent, or torch.cuda.Event
+    objects recorded by the library, which torch itself does not know were recorded)."""
     ms = C.c_float()
-    rc = _hip.hipEventElapsedTime(C.byref(ms), C.c_void_p(before.cuda_event), C.c_void_p(after.cuda_event))
+    rc = _hip_lib().hipEventElapsedTime(C.byref(ms), C.c_void_p(before.cuda_event), C.c_void_p(after.cuda_event))
     if rc != 0:
         raise RuntimeError(f"hipEventElapsedTime failed with hipError {rc}")
     return ms.value
+
+
+class TimingEvent:
+    """A HIP event for timing kernels only, on the current device: created with
+    hipEventDisableSystemFence, so that recording it (the library attaches it to a decode
+    kernel's dispatch) adds no system-scope cache writeback and invalidation to the stream
+    -- with the default flags each attached pair costs the stream a few microseconds.  Its
+    time is read (event_elapsed_ms) only after the device has been synchronised.  Exposes
+    the handle as ``cuda_event``, like torch.cuda.Event."""
+
+    def __init__(self):
+        h = C.c_void_p()
+        rc = _hip_lib().hipEventCreateWithFlags(C.byref(h), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0 or not h.value:
+            raise RuntimeError(f"hipEventCreateWithFlags failed with hipError {rc}")
+        self.cuda_event = h.value
+
+    def __del__(self):
+        if getattr(self, "cuda_event", 0) and _hip is not None:
+            _hip.hipEventDestroy(C.c_void_p(self.cuda_event))
+            self.cuda_event = 0
 
 
 def check(status: int, where: str):
