@@ -89,8 +89,10 @@ class DeltaStack:
         """One decode step.  q [L][B][Hq][D]; k_new, v_new [L][B][Hkv][D] (the cache's activation
         dtype: bfloat16 for bf16 and fp8 pools, float32 for f32 pools).
 
-        ``tracer`` (optional) has ``pair(layer, tier)`` returning a (before, after)
-        torch.cuda.Event pair to record around that layer's decode kernel, or None.
+        ``tracer`` (optional) has ``pair(layer, tier)`` returning a (before, after) pair
+        of timing events to attach to that layer's decode kernel (objects whose
+        ``cuda_event`` is a HIP event handle: ``_lib.TimingEvent`` or a recorded
+        torch.cuda.Event), or None.
         """
         c = self.c
         B = c.batch

@@ -130,3 +130,61 @@ def test_native_stack_step_equals_python_loop(kv):
     with pytest.raises(LakError, match="LAK_EINVAL"):
         st.step(z, zk, zk)
     assert cache.seq_lens_host() == [20]  # nothing ran, not even the step's length increment
+
+
+@pytest.mark.parametrize("native", [True, False])
+def test_traced_stack_times_every_decode_kernel(native):
+    """Events attached to the decode kernels (timing-only HIP events, as the benchmark
+    uses, and torch's default events) leave every output bit unchanged and give each
+    kernel a positive duration; one step's kernels fit inside that step's wall time."""
+    import time
+    from layer_aware_kv_amd import DeltaStack, PagedKVCache
+    from layer_aware_kv_amd._lib import TimingEvent, event_elapsed_ms
+    from workload.cases import random_case
+    L, B, HQ, HKV, D, P = 5, 2, 8, 2, 128, 16
+    lens = [700, 333]
+    tiers = ["full", "delta", "sparse", "sparse", "full"]
+
+    class Pairs:
+        def __init__(self, make):
+            self.make, self.records = make, []
+
+        def pair(self, layer, tier):
+            ev = (self.make(), self.make())
+            self.records.append((layer, tier, ev))
+            return ev
+
+    def torch_event():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()  # torch creates the HIP event at its first record
+        return e
+
+    runs = []
+    for make in (None, TimingEvent, torch_event):
+        cache = PagedKVCache(L, B, HQ, HKV, D, P, 64, 2 * 64, "bf16")
+        cache.seq_reset(lens, reserve_tokens=4)
+        for layer in range(L):
+            c = random_case(300 + layer, B, HQ, HKV, D, lens, "bf16")
+            cache.kv_prefill(layer, torch.from_numpy(c.K).to(torch.bfloat16).cuda(),
+                             torch.from_numpy(c.V).to(torch.bfloat16).cuda())
+        st = DeltaStack(cache, tiers, 4, 2, 0.09, native=native)
+        c = random_case(400, L * B, HQ, HKV, D, [1], "bf16")
+        q = torch.from_numpy(c.q).to(torch.bfloat16).cuda().view(L, B, HQ, D)
+        kn = torch.from_numpy(c.k_new).to(torch.bfloat16).cuda().view(L, B, HKV, D)
+        vn = torch.from_numpy(c.v_new).to(torch.bfloat16).cuda().view(L, B, HKV, D)
+        tr = Pairs(make) if make is not None else None
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        st.step(q, kn, vn, tr)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3
+        runs.append((st.out.clone(), st.lse.clone(), {l: v.clone() for l, v in st.sel.items()}))
+        if tr is not None:
+            assert [(l, t) for l, t, _ in tr.records] == list(enumerate(tiers))
+            ms = [event_elapsed_ms(*ev) for _, _, ev in tr.records]
+            print(make.__name__, [round(x * 1e3, 1) for x in ms], f"wall {wall_ms:.3f} ms", flush=True)
+            assert all(0.0 < x < wall_ms for x in ms)
+            assert sum(ms) < wall_ms
+    for o, l, s in runs[1:]:
+        assert torch.equal(o, runs[0][0]) and torch.equal(l, runs[0][1])
+        assert all(torch.equal(s[k], runs[0][2][k]) for k in s)
