@@ -77,8 +77,9 @@ int env_int(const char* name, int dflt, int lo, int hi) {
 
 int lak::tune_decode_batch(int mode) {
   static const int full = env_int("LAK_TUNE_DECODE_BATCH", 1, 1, 2);
-  static const int sparse = env_int("LAK_TUNE_SPARSE_BATCH", 1, 1, 4);
-  return mode == MODE_SPARSE ? (sparse == 3 ? 2 : sparse) : full;
+  static const int delta = env_int("LAK_TUNE_DELTA_BATCH", full, 1, 2);
+  static const int sparse = env_int("LAK_TUNE_SPARSE_BATCH", 0, 0, 4);  // 0: by the call's split size
+  return mode == MODE_SPARSE ? (sparse == 3 ? 2 : sparse) : (mode == MODE_DELTA ? delta : full);
 }
 
 int lak::tune_target_wgs(int mode) {

@@ -698,7 +698,15 @@ static hipError_t launch_decode_t(int mode, const DecodeArgs& a, int splits, int
   dim3 grid(splits, a.hkv, batch);
   // fp32 pools always load one sub-tile at a time: their fragments fill the register
   // budget of a deeper batch.
-  const int u = ESZ == 4 ? 1 : tune_decode_batch(mode);
+  int u = ESZ == 4 ? 1 : tune_decode_batch(mode);
+  if (u == 0) {
+    // sparse tier, by split size: a wave whose whole share is at most two sub-tiles loads
+    // it in one batch (one memory round trip per wave; a B 8, 16k-context stack +1.2%);
+    // longer shares keep one sub-tile per batch and the four waves per SIMD that hide
+    // their latency better (two per batch: B 16, 64k-context stack -1.3%)
+    const int per_wave = (a.pps + kWaves - 1) / kWaves * (a.page / kSub);
+    u = per_wave <= 2 ? 2 : 1;
+  }
   if constexpr (ESZ != 4) {
     if (u == 4) {
       launch_decode_u<ESZ, D, 4>(mode, a, grid, lds, st, ev0, ev1);

@@ -99,8 +99,11 @@ struct KvGeom {
 };
 
 // Tuning knobs, read once from the environment (defaults are the tuned values):
-//   LAK_TUNE_DECODE_BATCH  sub-tiles loaded together per wave, full / delta tiers (1 or 2)
-//   LAK_TUNE_SPARSE_BATCH  the same for the sparse tier (1, 2 or 4); fp32 pools always take 1
+//   LAK_TUNE_DECODE_BATCH  sub-tiles loaded together per wave, full tier (1 or 2)
+//   LAK_TUNE_DELTA_BATCH   the same for the delta tier (default: as the full tier)
+//   LAK_TUNE_SPARSE_BATCH  the same for the sparse tier (1, 2 or 4; 0, the default: 2 when a
+//                          wave's whole share is at most two sub-tiles, else 1); fp32 pools
+//                          always take 1
 //   LAK_TUNE_TARGET_WGS    workgroups a full / delta split-K launch aims for
 //   LAK_TUNE_SPARSE_WGS    workgroups a sparse split-K launch aims for
 //   LAK_TUNE_DELTA_WGS     workgroups a delta split-K launch aims for (default 1536)
