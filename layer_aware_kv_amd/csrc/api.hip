@@ -40,7 +40,13 @@ lak_status hip_fail(hipError_t e, const char* where) {
 // LAK_TUNE_TARGET_WGS overrides) and the fewest 16-token sub-tiles one workgroup
 // is given.
 constexpr int kTargetWgs = 1024;
-constexpr int kTargetWgsDelta = 1536;  // smaller delta splits spread the scratch writes
+// Delta tier: its LDS stage of a split's page-score scratch holds three workgroups per
+// CU, so the launch takes two or fewer rounds.  At batch 16, 64k context, G 7, 1280
+// workgroups (205 pages, a 52.5 KiB stage: the fewest that still fit three per CU) ran
+// the stack 0.8-0.9% faster than 1536 and 1152-1408 0.6-4% slower, alternated in one
+// process; with fp8 pools (half the bytes per page) 1536 measured ~1% faster than 1280.
+constexpr int kTargetWgsDelta = 1280;
+constexpr int kTargetWgsDeltaFp8 = 1536;
 // Ragged batches (the longest row more than 1.1x the mean) on the full and delta tiers:
 // splits of a uniform batch end together in one workgroup round, those of unequal rows
 // do not, and smaller splits then keep the CUs busy to the end (workload of 32 rows of
@@ -82,11 +88,12 @@ int lak::tune_decode_batch(int mode) {
   return mode == MODE_SPARSE ? (sparse == 3 ? 2 : sparse) : (mode == MODE_DELTA ? delta : full);
 }
 
-int lak::tune_target_wgs(int mode) {
+int lak::tune_target_wgs(int mode, bool fp8) {
   static const int full = env_int("LAK_TUNE_TARGET_WGS", kTargetWgs, 64, 65536);
   static const int sparse = env_int("LAK_TUNE_SPARSE_WGS", kTargetWgs, 64, 65536);
-  static const int delta = env_int("LAK_TUNE_DELTA_WGS", kTargetWgsDelta, 64, 65536);
-  return mode == MODE_SPARSE ? sparse : (mode == MODE_DELTA ? delta : full);
+  static const int delta = env_int("LAK_TUNE_DELTA_WGS", 0, 64, 65536);  // 0: by pool type
+  if (mode == MODE_DELTA) return delta ? delta : (fp8 ? kTargetWgsDeltaFp8 : kTargetWgsDelta);
+  return mode == MODE_SPARSE ? sparse : full;
 }
 
 int lak::tune_ragged_wgs() {
@@ -192,9 +199,9 @@ WsLayout ws_layout(const lak_cache* c) {
 // rows (per-row item counts summed: a ragged batch gives its long rows more splits),
 // `max_items` the longest row's count and `max_splits` the most splits a row may use
 // (the partial buffers hold max_splits per row).
-int plan_pps(int64_t work, int max_items, int max_splits, int subtiles_per_page, int mode, bool ragged) {
-  const int target = (ragged && mode != MODE_SPARSE) ? std::max(tune_ragged_wgs(), tune_target_wgs(mode))
-                                                     : tune_target_wgs(mode);
+int plan_pps(int64_t work, int max_items, int max_splits, int subtiles_per_page, int mode, bool ragged, bool fp8) {
+  const int target = (ragged && mode != MODE_SPARSE) ? std::max(tune_ragged_wgs(), tune_target_wgs(mode, fp8))
+                                                     : tune_target_wgs(mode, fp8);
   int pps = (int)((work + target - 1) / target);
   pps = std::max(pps, (max_items + max_splits - 1) / std::max(max_splits, 1));
   const int min_sub = tune_min_subtiles();
@@ -320,12 +327,14 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
   }
   // ragged: the longest row holds more than 1.1x the mean row's items
   const bool ragged = (int64_t)max_items * c->batch * d.num_kv_heads * 10 > work * 11;
-  const int pps = plan_pps(work, max_items, c->s_cap / std::max(c->batch, 1), spp, mode, ragged);
+  const int pps =
+      plan_pps(work, max_items, c->s_cap / std::max(c->batch, 1), spp, mode, ragged, d.dtype == LAK_FP8_E4M3);
   const int splits = (max_items + pps - 1) / pps;
   if ((int64_t)splits * c->batch > c->s_cap)
     return fail(LAK_EINVAL, "internal: %d splits x %d rows exceed capacity %d", splits, c->batch, c->s_cap);
   if (parts && partial_bytes(c, splits) > parts_cap)
-    return fail(LAK_EINVAL, "split partials need %zu bytes, more than the %zu-byte static scratch (batch %d, %d splits)",
+    return fail(LAK_EINVAL,
+                "split partials need %zu bytes, more than the %zu-byte static scratch (batch %d, %d splits)",
                 partial_bytes(c, splits), parts_cap, c->batch, splits);
 
   DecodeArgs a;
@@ -484,9 +493,9 @@ lak_status lak_cache_create(const lak_cache_desc* desc, lak_cache** out) {
   // at most M items) S <= target / R + 1, and with pps capped at kMaxItemsPerSplit
   // S <= M / kMaxItemsPerSplit + 1.
   {
-    const int tmax = std::max(std::max(std::max(tune_target_wgs(MODE_FULL), tune_target_wgs(MODE_SPARSE)),
-                                       tune_target_wgs(MODE_DELTA)),
-                              tune_ragged_wgs());
+    const int tiers = std::max(tune_target_wgs(MODE_FULL, false), tune_target_wgs(MODE_SPARSE, false));
+    const int delta = std::max(tune_target_wgs(MODE_DELTA, false), tune_target_wgs(MODE_DELTA, true));
+    const int tmax = std::max(std::max(tiers, delta), tune_ragged_wgs());
     c->s_cap = (tmax + d.num_kv_heads - 1) / d.num_kv_heads +
                d.max_batch * ((d.max_pages_per_seq + kMaxItemsPerSplit - 1) / kMaxItemsPerSplit + 2);
   }
@@ -715,9 +724,9 @@ lak_status lak_attn_full(lak_cache* c, int32_t layer, const void* q, const void*
 }
 
 lak_status lak_attn_delta_select(lak_cache* c, int32_t layer, const void* q, const void* k_new,
-                                 const void* v_new, float sm_scale, void* out, float* lse, int32_t k_top, int32_t recency, int32_t agg, int32_t scope,
-                                 int32_t* sel, int32_t* sel_count, int32_t sel_capacity, float* page_scores,
-                                 void* ws, size_t ws_bytes, void* stream) {
+                                 const void* v_new, float sm_scale, void* out, float* lse, int32_t k_top,
+                                 int32_t recency, int32_t agg, int32_t scope, int32_t* sel, int32_t* sel_count,
+                                 int32_t sel_capacity, float* page_scores, void* ws, size_t ws_bytes, void* stream) {
   lak_status s = check_cache(c, true);
   if (s != LAK_OK) return s;
   if ((s = check_layer(c, layer)) != LAK_OK) return s;
