@@ -36,10 +36,13 @@ lak_status hip_fail(hipError_t e, const char* where) {
   return fail(LAK_EHIP, "%s: %s", where, hipGetErrorString(e));
 }
 
-// Workgroups a split-K launch aims for (about 4 per compute unit on a 256-CU part;
-// LAK_TUNE_TARGET_WGS overrides) and the fewest 16-token sub-tiles one workgroup
-// is given.
-constexpr int kTargetWgs = 1024;
+// Workgroups a split-K launch aims for and the fewest 16-token sub-tiles one workgroup
+// is given.  Full tier: three per CU of a 256-CU part, one round (at batch 16, 64k
+// context the all-full stack ran 1.8% faster than at 1024 and 1-6% slower at 512, 640
+// and 896, alternated in one process; batch 8, 16k context 2.6% faster than 1024).
+// Sparse tier: four per CU (768 and 1536 were 0.4% and 2.2% slower at batch 16).
+constexpr int kTargetWgsFull = 768;
+constexpr int kTargetWgsSparse = 1024;
 // Delta tier: its LDS stage of a split's page-score scratch holds three workgroups per
 // CU, so the launch takes two or fewer rounds.  At batch 16, 64k context, G 7, 1280
 // workgroups (205 pages, a 52.5 KiB stage: the fewest that still fit three per CU) ran
@@ -89,8 +92,8 @@ int lak::tune_decode_batch(int mode) {
 }
 
 int lak::tune_target_wgs(int mode, bool fp8) {
-  static const int full = env_int("LAK_TUNE_TARGET_WGS", kTargetWgs, 64, 65536);
-  static const int sparse = env_int("LAK_TUNE_SPARSE_WGS", kTargetWgs, 64, 65536);
+  static const int full = env_int("LAK_TUNE_TARGET_WGS", kTargetWgsFull, 64, 65536);
+  static const int sparse = env_int("LAK_TUNE_SPARSE_WGS", kTargetWgsSparse, 64, 65536);
   static const int delta = env_int("LAK_TUNE_DELTA_WGS", 0, 64, 65536);  // 0: by pool type
   if (mode == MODE_DELTA) return delta ? delta : (fp8 ? kTargetWgsDeltaFp8 : kTargetWgsDelta);
   return mode == MODE_SPARSE ? sparse : full;

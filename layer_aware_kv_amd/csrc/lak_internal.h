@@ -104,8 +104,8 @@ struct KvGeom {
 //   LAK_TUNE_SPARSE_BATCH  the same for the sparse tier (1, 2 or 4; 0, the default: 2 when a
 //                          wave's whole share is at most two sub-tiles, else 1); fp32 pools
 //                          always take 1
-//   LAK_TUNE_TARGET_WGS    workgroups a full / delta split-K launch aims for
-//   LAK_TUNE_SPARSE_WGS    workgroups a sparse split-K launch aims for
+//   LAK_TUNE_TARGET_WGS    workgroups a full split-K launch aims for (default 768)
+//   LAK_TUNE_SPARSE_WGS    workgroups a sparse split-K launch aims for (default 1024)
 //   LAK_TUNE_DELTA_WGS     workgroups a delta split-K launch aims for (default 1280; 1536
 //                          with fp8 pools)
 //   LAK_TUNE_RAGGED_WGS    workgroups a full / delta launch over a ragged batch aims for (3072)
