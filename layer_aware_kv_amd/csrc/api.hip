@@ -43,13 +43,20 @@ lak_status hip_fail(hipError_t e, const char* where) {
 // Sparse tier: four per CU (768 and 1536 were 0.4% and 2.2% slower at batch 16).
 constexpr int kTargetWgsFull = 768;
 constexpr int kTargetWgsSparse = 1024;
-// Delta tier: its LDS stage of a split's page-score scratch holds three workgroups per
-// CU, so the launch takes two or fewer rounds.  At batch 16, 64k context, G 7, 1280
-// workgroups (205 pages, a 52.5 KiB stage: the fewest that still fit three per CU) ran
-// the stack 0.8-0.9% faster than 1536 and 1152-1408 0.6-4% slower, alternated in one
-// process; with fp8 pools (half the bytes per page) 1536 measured ~1% faster than 1280.
-constexpr int kTargetWgsDelta = 1280;
-constexpr int kTargetWgsDeltaFp8 = 1536;
+// Delta tier.  Where a split's LDS stage of page-score scratch limits a CU to fewer
+// than four workgroups (MAX aggregation at long contexts), the launch aims at the fewest
+// workgroups whose stage still leaves room for three; otherwise at 1.5 rounds of four
+// per CU (kTargetWgsDeltaLong) when that still gives a workgroup kDeltaLongMinSubtiles
+// sub-tiles, else at one round (kTargetWgsDeltaMin).  Alternated in one process: batch
+// 16, 64k context, G 7, MAX: 1280 workgroups (splits of up to 209 pages, a 53.5 KiB
+// stage) ran the stack 0.8-0.9% faster than 1536 and 0.6-4% faster than 1152-1408;
+// SUM (a small stage): 1536 0.6-2.7% faster than 1024-2048; batch 8, 16k context:
+// 1024 1.6% (MAX) and 2.9% (SUM) faster than 1536.
+constexpr int kTargetWgsDeltaMin = 1024;
+constexpr int kTargetWgsDeltaLong = 1536;
+constexpr int kDeltaLongMinSubtiles = 64;
+constexpr int kDeltaWgsPerCu = 3;
+constexpr size_t kLdsBytesPerCu = 160 * 1024;
 // Ragged batches (the longest row more than 1.1x the mean) on the full and delta tiers:
 // splits of a uniform batch end together in one workgroup round, those of unequal rows
 // do not, and smaller splits then keep the CUs busy to the end (workload of 32 rows of
@@ -91,12 +98,19 @@ int lak::tune_decode_batch(int mode) {
   return mode == MODE_SPARSE ? (sparse == 3 ? 2 : sparse) : (mode == MODE_DELTA ? delta : full);
 }
 
-int lak::tune_target_wgs(int mode, bool fp8) {
+int lak::tune_target_wgs(int mode, int64_t work, size_t stage_per_item, int subtiles_per_item) {
   static const int full = env_int("LAK_TUNE_TARGET_WGS", kTargetWgsFull, 64, 65536);
   static const int sparse = env_int("LAK_TUNE_SPARSE_WGS", kTargetWgsSparse, 64, 65536);
-  static const int delta = env_int("LAK_TUNE_DELTA_WGS", 0, 64, 65536);  // 0: by pool type
-  if (mode == MODE_DELTA) return delta ? delta : (fp8 ? kTargetWgsDeltaFp8 : kTargetWgsDelta);
-  return mode == MODE_SPARSE ? sparse : full;
+  static const int delta = env_int("LAK_TUNE_DELTA_WGS", 0, 64, 65536);  // 0: by the stage size
+  if (mode != MODE_DELTA) return mode == MODE_SPARSE ? sparse : full;
+  if (delta) return delta;
+  // stage bytes that leave room for three, less 1 KiB per workgroup for the allocation granularity
+  const size_t per_wg = kLdsBytesPerCu / kDeltaWgsPerCu - 1024;
+  const int64_t items = std::max<int64_t>(1, (int64_t)(per_wg / std::max<size_t>(stage_per_item, 1)));
+  const int64_t lds_wgs = (work + items - 1) / items;
+  if (lds_wgs > kTargetWgsDeltaMin) return (int)std::min<int64_t>(lds_wgs, 65536);
+  const int64_t subtiles = work * std::max(subtiles_per_item, 1);
+  return subtiles >= (int64_t)kTargetWgsDeltaLong * kDeltaLongMinSubtiles ? kTargetWgsDeltaLong : kTargetWgsDeltaMin;
 }
 
 int lak::tune_ragged_wgs() {
@@ -202,9 +216,10 @@ WsLayout ws_layout(const lak_cache* c) {
 // rows (per-row item counts summed: a ragged batch gives its long rows more splits),
 // `max_items` the longest row's count and `max_splits` the most splits a row may use
 // (the partial buffers hold max_splits per row).
-int plan_pps(int64_t work, int max_items, int max_splits, int subtiles_per_page, int mode, bool ragged, bool fp8) {
-  const int target = (ragged && mode != MODE_SPARSE) ? std::max(tune_ragged_wgs(), tune_target_wgs(mode, fp8))
-                                                     : tune_target_wgs(mode, fp8);
+int plan_pps(int64_t work, int max_items, int max_splits, int subtiles_per_page, int mode, bool ragged,
+             size_t stage_per_item) {
+  const int base = tune_target_wgs(mode, work, stage_per_item, subtiles_per_page);
+  const int target = (ragged && mode != MODE_SPARSE) ? std::max(tune_ragged_wgs(), base) : base;
   int pps = (int)((work + target - 1) / target);
   pps = std::max(pps, (max_items + max_splits - 1) / std::max(max_splits, 1));
   const int min_sub = tune_min_subtiles();
@@ -330,8 +345,9 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
   }
   // ragged: the longest row holds more than 1.1x the mean row's items
   const bool ragged = (int64_t)max_items * c->batch * d.num_kv_heads * 10 > work * 11;
-  const int pps =
-      plan_pps(work, max_items, c->s_cap / std::max(c->batch, 1), spp, mode, ragged, d.dtype == LAK_FP8_E4M3);
+  const int G = d.num_q_heads / d.num_kv_heads;
+  const size_t stage_per_item = delta_stage_bytes(1, d.page_size, G, agg == LAK_AGG_SUM);
+  const int pps = plan_pps(work, max_items, c->s_cap / std::max(c->batch, 1), spp, mode, ragged, stage_per_item);
   const int splits = (max_items + pps - 1) / pps;
   if ((int64_t)splits * c->batch > c->s_cap)
     return fail(LAK_EINVAL, "internal: %d splits x %d rows exceed capacity %d", splits, c->batch, c->s_cap);
@@ -378,12 +394,8 @@ lak_status run_attention(lak_cache* c, int layer, int mode, const void* q, const
     a.pairs = reinterpret_cast<float*>(wsb + w.delta);
     a.rel_blk = reinterpret_cast<uint8_t*>(wsb + w.delta);
   }
-  {
-    const int G = d.num_q_heads / d.num_kv_heads;
-    const size_t staged = delta_stage_bytes(pps, d.page_size, G, agg == LAK_AGG_SUM);
-    a.lds_stage = (mode == MODE_DELTA && tune_delta_lds() && staged <= 64 * 1024) ? 1 : 0;
-    a.sum_pairs = (mode == MODE_DELTA && agg == LAK_AGG_SUM) ? 1 : 0;
-  }
+  a.lds_stage = (mode == MODE_DELTA && tune_delta_lds() && pps * stage_per_item <= 64 * 1024) ? 1 : 0;
+  a.sum_pairs = (mode == MODE_DELTA && agg == LAK_AGG_SUM) ? 1 : 0;
   a.t_pad = (int64_t)d.max_pages_per_seq * d.page_size;
   e = launch_decode(d.dtype, mode, d.head_dim, a, splits, c->batch, st, c->trace_before, c->trace_after);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -496,9 +508,10 @@ lak_status lak_cache_create(const lak_cache_desc* desc, lak_cache** out) {
   // at most M items) S <= target / R + 1, and with pps capped at kMaxItemsPerSplit
   // S <= M / kMaxItemsPerSplit + 1.
   {
-    const int tiers = std::max(tune_target_wgs(MODE_FULL, false), tune_target_wgs(MODE_SPARSE, false));
-    const int delta = std::max(tune_target_wgs(MODE_DELTA, false), tune_target_wgs(MODE_DELTA, true));
-    const int tmax = std::max(std::max(tiers, delta), tune_ragged_wgs());
+    // (the delta tier's target grows with the call's work; where it passes this bound the
+    // split count is capped by the partial buffers and the splits grow instead)
+    const int tiers = std::max(tune_target_wgs(MODE_FULL, 0, 0, 1), tune_target_wgs(MODE_SPARSE, 0, 0, 1));
+    const int tmax = std::max(std::max(tiers, std::max(kTargetWgsDeltaLong, 2048)), tune_ragged_wgs());
     c->s_cap = (tmax + d.num_kv_heads - 1) / d.num_kv_heads +
                d.max_batch * ((d.max_pages_per_seq + kMaxItemsPerSplit - 1) / kMaxItemsPerSplit + 2);
   }

@@ -106,8 +106,9 @@ struct KvGeom {
 //                          always take 1
 //   LAK_TUNE_TARGET_WGS    workgroups a full split-K launch aims for (default 768)
 //   LAK_TUNE_SPARSE_WGS    workgroups a sparse split-K launch aims for (default 1024)
-//   LAK_TUNE_DELTA_WGS     workgroups a delta split-K launch aims for (default 1280; 1536
-//                          with fp8 pools)
+//   LAK_TUNE_DELTA_WGS     workgroups a delta split-K launch aims for (default: the fewest
+//                          whose LDS stage fits three per CU where the stage limits
+//                          occupancy, else 1536 for long calls and 1024 for short ones)
 //   LAK_TUNE_RAGGED_WGS    workgroups a full / delta launch over a ragged batch aims for (3072)
 //   LAK_TUNE_DELTA_LDS     1 (default): delta scratch staged in LDS, written at a split's end
 //   LAK_TUNE_MIN_SUBTILES  fewest 16-token sub-tiles a split-K workgroup is given (default 8)
@@ -126,7 +127,9 @@ inline size_t delta_stage_bytes(int pps, int page, int G, bool sum = false) {
   const size_t gp = (size_t)(G + (G & 1));
   return (size_t)pps * (page / 16) * (sum ? gp * 2 * 4 : (size_t)max_block_bytes(G));
 }
-int tune_target_wgs(int mode, bool fp8);
+// Workgroups a split-K launch of `mode` aims for; the delta tier's depends on the call's
+// total items `work`, the LDS stage bytes per item and the sub-tiles per item.
+int tune_target_wgs(int mode, int64_t work, size_t stage_per_item, int subtiles_per_item);
 int tune_topk_wave_kpl();
 int tune_score_tokens();
 int tune_ragged_wgs();
