@@ -56,7 +56,6 @@ constexpr int kTargetWgsDeltaMin = 1024;
 constexpr int kTargetWgsDeltaLong = 1536;
 constexpr int kDeltaLongMinSubtiles = 64;
 constexpr int kDeltaWgsPerCu = 3;
-constexpr size_t kLdsBytesPerCu = 160 * 1024;
 // Ragged batches (the longest row more than 1.1x the mean) on the full and delta tiers:
 // splits of a uniform batch end together in one workgroup round, those of unequal rows
 // do not, and smaller splits then keep the CUs busy to the end (workload of 32 rows of
@@ -92,9 +91,10 @@ int env_int(const char* name, int dflt, int lo, int hi) {
 }  // namespace
 
 int lak::tune_decode_batch(int mode) {
+  // 0: chosen per launch (launch_decode_t)
   static const int full = env_int("LAK_TUNE_DECODE_BATCH", 1, 1, 2);
-  static const int delta = env_int("LAK_TUNE_DELTA_BATCH", full, 1, 2);
-  static const int sparse = env_int("LAK_TUNE_SPARSE_BATCH", 0, 0, 4);  // 0: by the call's split size
+  static const int delta = env_int("LAK_TUNE_DELTA_BATCH", 0, 0, 2);
+  static const int sparse = env_int("LAK_TUNE_SPARSE_BATCH", 0, 0, 4);
   return mode == MODE_SPARSE ? (sparse == 3 ? 2 : sparse) : (mode == MODE_DELTA ? delta : full);
 }
 

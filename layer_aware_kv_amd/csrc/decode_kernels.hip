@@ -700,12 +700,24 @@ static hipError_t launch_decode_t(int mode, const DecodeArgs& a, int splits, int
   // budget of a deeper batch.
   int u = ESZ == 4 ? 1 : tune_decode_batch(mode);
   if (u == 0) {
-    // sparse tier, by split size: a wave whose whole share is at most two sub-tiles loads
-    // it in one batch (one memory round trip per wave; a B 8, 16k-context stack +1.2%);
-    // longer shares keep one sub-tile per batch and the four waves per SIMD that hide
-    // their latency better (two per batch: B 16, 64k-context stack -1.3%)
-    const int per_wave = (a.pps + kWaves - 1) / kWaves * (a.page / kSub);
-    u = per_wave <= 2 ? 2 : 1;
+    if (ESZ == 1 && (mode == MODE_SPARSE || (mode == MODE_DELTA && 4 * lds > kLdsBytesPerCu))) {
+      // fp8 pools (half the bytes and registers per sub-tile): two sub-tiles per batch on
+      // the sparse tier, and on the delta tier where its LDS stage already holds a CU to
+      // three workgroups, so the deeper batch's registers cost no occupancy (B 16,
+      // 64k-context stack +0.4% and +1.8%; at B 8, 16k context, where the delta stage is
+      // small, the delta tier's two per batch cost 5%; the full tier keeps one: two cost
+      // it 0.7%)
+      u = 2;
+    } else if (mode == MODE_SPARSE) {
+      // sparse tier, by split size: a wave whose whole share is at most two sub-tiles loads
+      // it in one batch (one memory round trip per wave; a B 8, 16k-context stack +1.2%);
+      // longer shares keep one sub-tile per batch and the four waves per SIMD that hide
+      // their latency better (two per batch: B 16, 64k-context stack -1.3%)
+      const int per_wave = (a.pps + kWaves - 1) / kWaves * (a.page / kSub);
+      u = per_wave <= 2 ? 2 : 1;
+    } else {
+      u = 1;  // bfloat16 delta tier: two per batch cost the B 16, 64k-context stack 1.0%
+    }
   }
   if constexpr (ESZ != 4) {
     if (u == 4) {

@@ -8,6 +8,8 @@ namespace lak {
 
 enum Mode { MODE_FULL = 0, MODE_DELTA = 1, MODE_SPARSE = 2 };
 
+constexpr size_t kLdsBytesPerCu = 160 * 1024;  // LDS of one gfx950 compute unit
+
 // Arguments of the split-K decode kernel (all three tiers).
 struct DecodeArgs {
   const void* k_pool;
@@ -100,10 +102,11 @@ struct KvGeom {
 
 // Tuning knobs, read once from the environment (defaults are the tuned values):
 //   LAK_TUNE_DECODE_BATCH  sub-tiles loaded together per wave, full tier (1 or 2)
-//   LAK_TUNE_DELTA_BATCH   the same for the delta tier (default: as the full tier)
-//   LAK_TUNE_SPARSE_BATCH  the same for the sparse tier (1, 2 or 4; 0, the default: 2 when a
-//                          wave's whole share is at most two sub-tiles, else 1); fp32 pools
-//                          always take 1
+//   LAK_TUNE_DELTA_BATCH   the same for the delta tier (1 or 2; 0, the default: 2 with fp8
+//                          pools where the LDS stage limits a CU to three workgroups, else 1)
+//   LAK_TUNE_SPARSE_BATCH  the same for the sparse tier (1, 2 or 4; 0, the default: 2 with
+//                          fp8 pools or when a wave's whole share is at most two sub-tiles,
+//                          else 1); fp32 pools always take 1
 //   LAK_TUNE_TARGET_WGS    workgroups a full split-K launch aims for (default 768)
 //   LAK_TUNE_SPARSE_WGS    workgroups a sparse split-K launch aims for (default 1024)
 //   LAK_TUNE_DELTA_WGS     workgroups a delta split-K launch aims for (default: the fewest
