@@ -68,7 +68,15 @@ constexpr int kMinSubtilesPerWg = 8;
 // workgroup round (4097 pages: 16 splits of 257 instead of 17 of 256).
 constexpr int kMaxItemsPerSplit = 256;
 constexpr int kMaxItemsPerSplitFull = 512;
-constexpr int kScoreTokensPerBlock = 4096;  // 18.7 -> 17.9 us per delta layer at B 16, T 64k (2048, 8192 slower)
+// MAX page scoring: a block takes 1024-4096 consecutive tokens of a score row, as many as
+// keep the launch near kScoreTargetWgs blocks.  Alternated in one process: batch 8, 16k
+// context (512 blocks at 1024 tokens) ran the stack 2.0% faster than at 4096 (128
+// blocks); batch 16, 64k context stays at 4096 (1024 blocks; 18.7 -> 17.9 us per delta
+// layer against 2048 across processes, equal in one); batch 32 ragged to 32k stays at
+// 4096 (1024 tokens: 1.6% slower).
+constexpr int kScoreTokensMin = 1024;
+constexpr int kScoreTokensMax = 4096;
+constexpr int kScoreTargetWgs = 1024;
 
 int esize(int dtype) { return dtype == LAK_BF16 ? 2 : (dtype == LAK_FP8_E4M3 ? 1 : 4); }
 
@@ -123,10 +131,13 @@ int lak::tune_min_subtiles() {
   return v;
 }
 
-int lak::tune_score_tokens() {
+int lak::tune_score_tokens(int64_t row_tokens) {
   // whole rounds of 256 threads x 4 tokens, so that no page straddles two blocks (P <= 64)
-  static const int v = env_int("LAK_TUNE_SCORE_TOKENS", kScoreTokensPerBlock, 1024, 65536);
-  return v - v % 1024;
+  static const int v = env_int("LAK_TUNE_SCORE_TOKENS", 0, 1024, 65536);  // 0: by the call's size
+  if (v) return v - v % 1024;
+  const int64_t per = (row_tokens + kScoreTargetWgs - 1) / kScoreTargetWgs;
+  const int64_t t = (per + 1023) / 1024 * 1024;
+  return (int)std::min<int64_t>(kScoreTokensMax, std::max<int64_t>(kScoreTokensMin, t));
 }
 
 int lak::tune_topk_wave_kpl() {
@@ -772,7 +783,9 @@ lak_status lak_attn_delta_select(lak_cache* c, int32_t layer, const void* q, con
   pa.max_pages = c->d.max_pages_per_seq;
   pa.agg = agg;
   pa.scope = scope;
-  pa.tokens_per_block = tune_score_tokens();
+  // score rows x the longest row's tokens: the scoring launch's extent
+  pa.tokens_per_block = tune_score_tokens((int64_t)c->batch * (scope == LAK_SCOPE_GROUP ? c->d.num_kv_heads : 1) *
+                                          c->max_np() * c->d.page_size);
   const int rows = scope == LAK_SCOPE_GROUP ? c->d.num_kv_heads : 1;
   hipError_t e = launch_delta_post(c->d.dtype, c->d.head_dim, pa, c->batch, rows, c->max_np(), st);
   if (e != hipSuccess) return hip_fail(e, "delta post launch");

@@ -115,7 +115,8 @@ struct KvGeom {
 //   LAK_TUNE_RAGGED_WGS    workgroups a full / delta launch over a ragged batch aims for (3072)
 //   LAK_TUNE_DELTA_LDS     1 (default): delta scratch staged in LDS, written at a split's end
 //   LAK_TUNE_MIN_SUBTILES  fewest 16-token sub-tiles a split-K workgroup is given (default 8)
-//   LAK_TUNE_SCORE_TOKENS  tokens of one score row per MAX page-scoring block (default 4096)
+//   LAK_TUNE_SCORE_TOKENS  tokens of one score row per MAX page-scoring block (default: 1024
+//                          to 4096, as many as keep the launch near 1024 blocks)
 //   LAK_TUNE_TOPK_WAVE_KPL  largest candidate row (in 64-page units) that the one-wave
 //                          selector takes (0, the default: the workgroup selector always)
 int tune_decode_batch(int mode);
@@ -134,7 +135,8 @@ inline size_t delta_stage_bytes(int pps, int page, int G, bool sum = false) {
 // total items `work`, the LDS stage bytes per item and the sub-tiles per item.
 int tune_target_wgs(int mode, int64_t work, size_t stage_per_item, int subtiles_per_item);
 int tune_topk_wave_kpl();
-int tune_score_tokens();
+// Tokens of a score row per MAX page-scoring block, for `row_tokens` tokens in all rows.
+int tune_score_tokens(int64_t row_tokens);
 int tune_ragged_wgs();
 int tune_delta_lds();
 int tune_min_subtiles();
